@@ -1,0 +1,216 @@
+/*
+ * sp24.h -- C ABI of libsp24.so: 2:4 semi-structured sparsity on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (sources: "2:4 Structured Sparsity Explained", sections "How
+ * 2:4 sparsity works" and "How to make a model 2:4 sparse"; "Production 2:4
+ * Structured Sparsity for LLMs", sections "From Unstructured Pruning to
+ * Hardware-Accelerable Sparsity" and "Sparse Tactic Audit"; the
+ * 2:4-versus-quantization paper, section 2 "Sparse tensor cores" and
+ * section 3.5 "Measuring speed"):
+ *
+ *   - a 2:4 operand keeps, in every group of 4 consecutive elements along the
+ *     reduction axis K, the 2 elements of largest magnitude (ties: the lower
+ *     index wins) and stores them in half the space, plus a 2-bit position
+ *     (0..3) for each kept value;
+ *   - a sparse MMA multiplies that compressed first operand by a dense second
+ *     operand, the positions selecting the matching dense elements, for up
+ *     to twice the dense rate;
+ *   - a dense GEMM runs on the same shapes, and a per-shape tactic keeps
+ *     whichever is faster, falling back to dense when sparse is not.
+ *
+ * Conventions shared by every call
+ *   - All tensors are row-major with K contiguous.  W is (N, K), X is (M, K),
+ *     Y = X * W^T is (M, N).  "rows" of a compressed operand is N for W and M
+ *     for X.
+ *   - Compressed form of a rows x K operand:
+ *       values : rows x K/2 elements of the operand's dtype, row stride K/2.
+ *                Group g of row r stores its two kept elements at
+ *                values[r][2g] (lower position p0) and values[r][2g+1]
+ *                (higher position p1), bit-for-bit copies of the input.
+ *       meta   : rows x ceil(K/32) uint32 words, row stride ceil(K/32).
+ *                Group g is the nibble p0 | p1 << 2 (p0 < p1) at bits
+ *                4*(g%8) .. 4*(g%8)+3 of meta[r][g/8]; nibbles past the last
+ *                group of a row are 0.  Only the six nibbles 0x4, 0x8, 0xC,
+ *                0x9, 0xD, 0xE occur.
+ *   - Magnitude is the integer value of the sign-stripped bit pattern; +0
+ *     and -0 tie, NaN ranks above Inf.  Dropped positions decompress to +0.
+ *   - fp8 is OCP E4M3 (e4m3fn).  A GEMM takes an optional fp32 scale per row
+ *     of X (per token) and per row of W (per output channel), NULL meaning 1:
+ *     Y[m][n] = (sum_k x[m][k] * w[n][k]) * scale_x[m] * scale_w[n]
+ *     ("FP8 (E4M3) needs only one scale per row or channel": the paper's
+ *     section 2, "Quantization").
+ *   - Accumulation is fp32; the output is rounded once, to nearest even.
+ *   - Every pointer argument is a device pointer unless marked "host".  The
+ *     caller allocates and owns every buffer; the library keeps no device
+ *     memory and holds no global mutable state (calls are thread-safe).
+ *   - Every call validates its arguments on the host before any HIP call and
+ *     returns an sp24_status without touching the device on failure.  Work
+ *     is enqueued asynchronously on `stream` (0 = the null stream); only
+ *     sp24_select_tactic synchronizes.  Device faults surface at the
+ *     caller's next synchronization.  No C++ exception crosses this ABI.
+ */
+#ifndef SP24_H
+#define SP24_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SP24_F16 = 0,   /* IEEE binary16 */
+    SP24_BF16 = 1,  /* bfloat16 */
+    SP24_E4M3 = 2,  /* OCP FP8 E4M3 (e4m3fn) */
+    SP24_F32 = 3    /* binary32: an output dtype only */
+} sp24_dtype;
+
+typedef enum {
+    SP24_SPARSE_W = 0, /* the weight W (N, K) is the compressed operand (static weights) */
+    SP24_SPARSE_X = 1  /* the activation X (M, K) is the compressed operand (dynamic) */
+} sp24_operand;
+
+typedef enum {
+    SP24_OK = 0,
+    SP24_E_NULL = 1,     /* a required pointer is NULL */
+    SP24_E_SHAPE = 2,    /* a size is negative, K % 4 != 0, or a leading dimension < K */
+    SP24_E_DTYPE = 3,    /* unsupported dtype or dtype combination */
+    SP24_E_ALIGN = 4,    /* pointer not 16-byte aligned, or K not a multiple of the GEMM's K tile */
+    SP24_E_HIP = 5       /* the HIP runtime reported an error (launch, event, device query) */
+} sp24_status;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *sp24_status_str(sp24_status s);
+
+/* Library version string, e.g. "sp24 0.1.0 gfx950" (static storage). */
+const char *sp24_version(void);
+
+/* Words of metadata per row: ceil(K / 32). */
+int64_t sp24_meta_words_per_row(int64_t K);
+
+/*
+ * Prune + compress ("2:4 Structured Sparsity Explained", "How to make a model
+ * 2:4 sparse": keep the two largest magnitudes of each group of four; and
+ * "How 2:4 sparsity works": half-size values plus a 2-bit index per kept
+ * value).  One pass: the dense operand is read once, values and meta are
+ * written once (the fused form of the paper's section 3.5).
+ *   dt      SP24_F16, SP24_BF16 or SP24_E4M3
+ *   rows, K dense operand is rows x K; K % 4 == 0; rows, K >= 0 (0 is a no-op)
+ *   src     rows x K, row stride ld_src elements (ld_src >= K)
+ *   values  out: rows x K/2 elements (dt), row stride K/2
+ *   meta    out: rows x ceil(K/32) uint32, row stride ceil(K/32)
+ * Misaligned pointers or strides are accepted (a slower kernel runs).
+ */
+sp24_status sp24_prune_compress(sp24_dtype dt, int64_t rows, int64_t K,
+                                const void *src, int64_t ld_src,
+                                void *values, uint32_t *meta, hipStream_t stream);
+
+/*
+ * Decompress: the inverse of sp24_prune_compress ("Production 2:4 Structured
+ * Sparsity for LLMs", playbook step 2: the dense view has exactly two zeros
+ * in every four along the reduction axis).  Every position of dst is
+ * written: +0 where a group dropped an element, the kept value (bit copy)
+ * elsewhere.  For an illegal nibble (p0 >= p1, never produced by
+ * sp24_prune_compress) value 0 is written at p0 and then value 1 at p1.
+ *   dst     out: rows x K, row stride ld_dst elements (ld_dst >= K)
+ */
+sp24_status sp24_decompress(sp24_dtype dt, int64_t rows, int64_t K,
+                            const void *values, const uint32_t *meta,
+                            void *dst, int64_t ld_dst, hipStream_t stream);
+
+/*
+ * Sparse x dense GEMM, Y = X * W^T (the paper's section 2 "Sparse tensor
+ * cores": the compressed first operand and its indices select the matching
+ * elements of the dense operand).
+ *   which     SP24_SPARSE_W: (values, meta) is W (N x K) compressed and
+ *             `dense` is X (M x K).  SP24_SPARSE_X: (values, meta) is X
+ *             compressed and `dense` is W.
+ *   in_dt     SP24_F16, SP24_BF16 or SP24_E4M3 (both operands)
+ *   out_dt    SP24_F16 or SP24_BF16 or SP24_F32 for 16-bit inputs;
+ *             SP24_BF16 or SP24_F32 for SP24_E4M3
+ *   M, N, K   M, N >= 0; K % 64 == 0 (16-bit) or K % 128 == 0 (fp8), else
+ *             SP24_E_ALIGN: the shape is not eligible and the caller runs
+ *             dense_gemm instead (a visible fallback, never a silent one)
+ *   scale_x   M fp32 per-token scales, or NULL (= 1); used with fp8 inputs
+ *   scale_w   N fp32 per-channel scales, or NULL (= 1); used with fp8 inputs
+ *   Y         out: M x N of out_dt, row stride N
+ *   All pointers 16-byte aligned.
+ */
+sp24_status sp24_gemm(sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt,
+                      int64_t M, int64_t N, int64_t K,
+                      const void *values, const uint32_t *meta, const void *dense,
+                      const float *scale_x, const float *scale_w,
+                      void *Y, hipStream_t stream);
+
+/*
+ * Dense GEMM on the same shapes, Y = X * W^T: the baseline every sparse
+ * tactic is timed against and the target of every fallback ("Production
+ * 2:4 Structured Sparsity for LLMs", section "Dense Fallback and Hybrid
+ * Sparsity Design").  Same dtypes, scales and layout as sp24_gemm.  It
+ * accepts every K that fills whole 16-byte chunks of a row, K % 8 == 0
+ * (16-bit) or K % 16 == 0 (fp8), so that it can take the shapes the sparse
+ * path rejects; else SP24_E_ALIGN.  Pointers 16-byte aligned.
+ */
+sp24_status dense_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K,
+                       const void *X, const void *W,
+                       const float *scale_x, const float *scale_w,
+                       void *Y, hipStream_t stream);
+
+/* Per-shape tactic record ("Production 2:4 Structured Sparsity for LLMs",
+ * section "Sparse Tactic Audit": eligible / selected / reason per layer). */
+typedef struct {
+    int eligible;          /* 1 if the sparse path accepts this shape and dtype */
+    int selected;          /* 1 = sparse, 0 = dense */
+    double t_sparse_us;    /* median device time of the sparse GEMM */
+    double t_compress_us;  /* median device time of prune+compress (SP24_SPARSE_X only, else 0) */
+    double t_dense_us;     /* median device time of the dense GEMM */
+    double ratio;          /* t_dense / median(t_compress + t_sparse per rep); > 1: sparse faster */
+    char reason[96];       /* why the choice was made, e.g. "Dense kernel 1.15x faster" */
+    char kernel[64];       /* name of the kernel that the chosen path actually launches */
+} sp24_tactic;
+
+/*
+ * Times the sparse path (for SP24_SPARSE_X: prune+compress of X, then the
+ * sparse GEMM; each side pays for producing its own input) against the dense
+ * path on the caller's buffers and chooses sparse iff its median time is
+ * strictly lower ("Production 2:4 Structured Sparsity for LLMs", section
+ * "Sparse Tactic Audit": latency is the sole criterion; a dense kernel that
+ * runs faster is chosen).
+ *   values, meta   compressed operand (SP24_SPARSE_W), or scratch of the
+ *                  compressed size that the timed compress overwrites
+ *                  (SP24_SPARSE_X)
+ *   dense_other    the operand that stays dense in the sparse path
+ *   dense_pruned   the dense (pruned) form of the sparse operand, used by the
+ *                  dense path (for SP24_SPARSE_X: the dense X that is
+ *                  compressed on every sparse call)
+ *   Y_scratch      M x N of out_dt, overwritten
+ *   warmup, reps   untimed and timed repetitions of each path (reps >= 1)
+ *   out            host: the record
+ * An ineligible shape or dtype yields SP24_OK with eligible = 0, selected = 0,
+ * reason "Alignment failure" or "Unsupported dtype", and only the dense path
+ * timed.  Synchronizes `stream`.
+ */
+sp24_status sp24_select_tactic(sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt,
+                               int64_t M, int64_t N, int64_t K,
+                               const void *values, const uint32_t *meta,
+                               const void *dense_other, const void *dense_pruned,
+                               const float *scale_x, const float *scale_w, void *Y_scratch,
+                               int warmup, int reps, hipStream_t stream, sp24_tactic *out);
+
+/*
+ * The decision rule alone, on host arrays of per-repetition times in
+ * microseconds (a pure host function: no HIP call).  t_sparse holds
+ * sparse(+compress) times, t_dense dense times; ns, nd >= 1 when eligible.
+ * Fills selected, t_sparse_us (median), t_dense_us (median), ratio and
+ * reason; leaves kernel and t_compress_us untouched.
+ */
+sp24_status sp24_tactic_decide(int eligible, const double *t_sparse, int ns,
+                               const double *t_dense, int nd, sp24_tactic *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SP24_H */

@@ -1,0 +1,351 @@
+// api.hip -- the extern "C" entry points of libsp24.so: argument
+// validation (on the host, before any HIP call), dispatch to the kernels,
+// and the sparse-versus-dense tactic selection.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "sp24_internal.h"
+
+#define SP24_API extern "C" __attribute__((visibility("default")))
+
+namespace sp24 {
+namespace {
+
+__global__ void fill_zero(uint8_t* p, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (; i < n; i += stride)
+        p[i] = 0;
+}
+
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s) {
+    if (bytes <= 0)
+        return hipSuccess;
+    int64_t blocks = std::min<int64_t>((bytes + 255) / 256, 4096);
+    hipLaunchKernelGGL(fill_zero, dim3((uint32_t)blocks), dim3(256), 0, s, (uint8_t*)p, bytes);
+    return hipGetLastError();
+}
+
+bool is_input_dtype(int dt) { return dt == SP24_F16 || dt == SP24_BF16 || dt == SP24_E4M3; }
+
+bool out_ok(sp24_dtype in, sp24_dtype out) {
+    if (in == SP24_E4M3)
+        return out == SP24_BF16 || out == SP24_F32;
+    return out == SP24_F16 || out == SP24_BF16 || out == SP24_F32;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shared checks of the two GEMM entry points.  Returns SP24_OK when the
+// shape is eligible for the MFMA kernels.
+sp24_status check_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K,
+                       std::initializer_list<const void*> required, const void* Y,
+                       const float* sx, const float* sw, bool sparse) {
+    if (!is_input_dtype(in_dt) || !out_ok(in_dt, out_dt))
+        return SP24_E_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0)
+        return SP24_E_SHAPE;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2)
+        return SP24_E_SHAPE;
+    if (M == 0 || N == 0)
+        return SP24_OK;
+    if (!Y)
+        return SP24_E_NULL;
+    if (K > 0)
+        for (const void* p : required)
+            if (!p)
+                return SP24_E_NULL;
+    // sparse: whole MFMA steps; dense: whole 16-byte chunks of every row
+    if (K % (sparse ? gemm_k_tile(in_dt) : 16 / elem_bytes(in_dt)) != 0)
+        return SP24_E_ALIGN;
+    if (!aligned16(Y) || ((uintptr_t)sx & 3u) || ((uintptr_t)sw & 3u))
+        return SP24_E_ALIGN;
+    for (const void* p : required)
+        if (!aligned16(p))
+            return SP24_E_ALIGN;
+    return SP24_OK;
+}
+
+double median(std::vector<double> v) {
+    if (v.empty())
+        return 0.0;
+    std::sort(v.begin(), v.end());
+    size_t n = v.size();
+    return n % 2 ? v[n / 2] : 0.5 * (v[n / 2 - 1] + v[n / 2]);
+}
+
+}  // namespace
+}  // namespace sp24
+
+using namespace sp24;
+
+SP24_API const char* sp24_status_str(sp24_status s) {
+    switch (s) {
+    case SP24_OK: return "SP24_OK";
+    case SP24_E_NULL: return "SP24_E_NULL: a required pointer is NULL";
+    case SP24_E_SHAPE: return "SP24_E_SHAPE: negative size, K % 4 != 0, or leading dimension < K";
+    case SP24_E_DTYPE: return "SP24_E_DTYPE: unsupported dtype or dtype combination";
+    case SP24_E_ALIGN: return "SP24_E_ALIGN: pointer not 16-byte aligned or K not a multiple of the GEMM K tile";
+    case SP24_E_HIP: return "SP24_E_HIP: the HIP runtime reported an error";
+    }
+    return "unknown sp24_status";
+}
+
+SP24_API const char* sp24_version(void) { return "sp24 0.1.0 gfx950"; }
+
+SP24_API int64_t sp24_meta_words_per_row(int64_t K) { return K < 0 ? 0 : meta_words(K); }
+
+SP24_API sp24_status sp24_prune_compress(sp24_dtype dt, int64_t rows, int64_t K, const void* src,
+                                         int64_t ld_src, void* values, uint32_t* meta,
+                                         hipStream_t stream) {
+    if (!is_input_dtype(dt))
+        return SP24_E_DTYPE;
+    if (rows < 0 || K < 0 || K % 4 != 0 || ld_src < K)
+        return SP24_E_SHAPE;
+    if (rows == 0 || K == 0)
+        return SP24_OK;
+    if (!src || !values || !meta)
+        return SP24_E_NULL;
+    return launch_prune_compress(dt, rows, K, src, ld_src, values, meta, stream) == hipSuccess
+               ? SP24_OK : SP24_E_HIP;
+}
+
+SP24_API sp24_status sp24_decompress(sp24_dtype dt, int64_t rows, int64_t K, const void* values,
+                                     const uint32_t* meta, void* dst, int64_t ld_dst,
+                                     hipStream_t stream) {
+    if (!is_input_dtype(dt))
+        return SP24_E_DTYPE;
+    if (rows < 0 || K < 0 || K % 4 != 0 || ld_dst < K)
+        return SP24_E_SHAPE;
+    if (rows == 0 || K == 0)
+        return SP24_OK;
+    if (!values || !meta || !dst)
+        return SP24_E_NULL;
+    return launch_decompress(dt, rows, K, values, meta, dst, ld_dst, stream) == hipSuccess
+               ? SP24_OK : SP24_E_HIP;
+}
+
+static sp24_status gemm_impl(sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt, int64_t M,
+                             int64_t N, int64_t K, const void* values, const uint32_t* meta,
+                             const void* dense, const float* scale_x, const float* scale_w, void* Y,
+                             hipStream_t stream, const char** kname) {
+    if (which != SP24_SPARSE_W && which != SP24_SPARSE_X)
+        return SP24_E_SHAPE;
+    sp24_status st = check_gemm(in_dt, out_dt, M, N, K, {values, meta, dense}, Y, scale_x, scale_w, true);
+    if (st != SP24_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return SP24_OK;
+    if (K == 0) {
+        if (kname) *kname = "fill_zero";
+        return launch_fill_zero(Y, M * N * elem_bytes(out_dt), stream) == hipSuccess ? SP24_OK : SP24_E_HIP;
+    }
+    GemmArgs g;
+    g.in_dt = in_dt;
+    g.out_dt = out_dt;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.a_vals = values;
+    g.a_meta = meta;
+    g.b = dense;
+    g.a_is_w = which == SP24_SPARSE_W;
+    g.scale_a = g.a_is_w ? scale_w : scale_x;
+    g.scale_b = g.a_is_w ? scale_x : scale_w;
+    g.Y = Y;
+    return launch_sp24_gemm(g, stream, kname) == hipSuccess ? SP24_OK : SP24_E_HIP;
+}
+
+static sp24_status dense_impl(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K,
+                              const void* X, const void* W, const float* scale_x, const float* scale_w,
+                              void* Y, hipStream_t stream, const char** kname) {
+    sp24_status st = check_gemm(in_dt, out_dt, M, N, K, {X, W}, Y, scale_x, scale_w, false);
+    if (st != SP24_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return SP24_OK;
+    if (K == 0) {
+        if (kname) *kname = "fill_zero";
+        return launch_fill_zero(Y, M * N * elem_bytes(out_dt), stream) == hipSuccess ? SP24_OK : SP24_E_HIP;
+    }
+    DenseArgs g;
+    g.in_dt = in_dt;
+    g.out_dt = out_dt;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.X = X;
+    g.W = W;
+    g.scale_x = scale_x;
+    g.scale_w = scale_w;
+    g.Y = Y;
+    return launch_dense_gemm(g, stream, kname) == hipSuccess ? SP24_OK : SP24_E_HIP;
+}
+
+SP24_API sp24_status sp24_gemm(sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt, int64_t M,
+                               int64_t N, int64_t K, const void* values, const uint32_t* meta,
+                               const void* dense, const float* scale_x, const float* scale_w, void* Y,
+                               hipStream_t stream) {
+    return gemm_impl(which, in_dt, out_dt, M, N, K, values, meta, dense, scale_x, scale_w, Y, stream, nullptr);
+}
+
+SP24_API sp24_status dense_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K,
+                                const void* X, const void* W, const float* scale_x,
+                                const float* scale_w, void* Y, hipStream_t stream) {
+    return dense_impl(in_dt, out_dt, M, N, K, X, W, scale_x, scale_w, Y, stream, nullptr);
+}
+
+SP24_API sp24_status sp24_tactic_decide(int eligible, const double* t_sparse, int ns, const double* t_dense,
+                                        int nd, sp24_tactic* out) {
+    if (!out)
+        return SP24_E_NULL;
+    if (nd < 1 || !t_dense || (eligible && (ns < 1 || !t_sparse)))
+        return SP24_E_SHAPE;
+    out->eligible = eligible ? 1 : 0;
+    out->t_dense_us = median(std::vector<double>(t_dense, t_dense + nd));
+    if (!eligible) {
+        out->selected = 0;
+        out->t_sparse_us = 0.0;
+        out->ratio = 0.0;
+        if (out->reason[0] == '\0')
+            snprintf(out->reason, sizeof(out->reason), "Not eligible");
+        return SP24_OK;
+    }
+    out->t_sparse_us = median(std::vector<double>(t_sparse, t_sparse + ns));
+    const double ts = out->t_sparse_us;
+    out->ratio = ts > 0.0 ? out->t_dense_us / ts : 0.0;
+    // latency is the sole criterion: sparse only if strictly faster
+    out->selected = ts < out->t_dense_us ? 1 : 0;
+    if (out->selected)
+        snprintf(out->reason, sizeof(out->reason), "Sparse kernel %.2fx faster", out->ratio);
+    else if (ts == out->t_dense_us)
+        snprintf(out->reason, sizeof(out->reason), "Tie: dense kept (sparse not faster)");
+    else
+        snprintf(out->reason, sizeof(out->reason), "Dense kernel %.2fx faster", ts / out->t_dense_us);
+    return SP24_OK;
+}
+
+SP24_API sp24_status sp24_select_tactic(sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt, int64_t M,
+                                        int64_t N, int64_t K, const void* values, const uint32_t* meta,
+                                        const void* dense_other, const void* dense_pruned,
+                                        const float* scale_x, const float* scale_w, void* Y_scratch,
+                                        int warmup, int reps, hipStream_t stream, sp24_tactic* out) {
+    if (!out)
+        return SP24_E_NULL;
+    memset(out, 0, sizeof(*out));
+    if (reps < 1 || warmup < 0)
+        return SP24_E_SHAPE;
+    if (which != SP24_SPARSE_W && which != SP24_SPARSE_X)
+        return SP24_E_SHAPE;
+    // eligibility of the sparse path
+    int eligible = 1;
+    if (!is_input_dtype(in_dt) || !out_ok(in_dt, out_dt)) {
+        eligible = 0;
+        snprintf(out->reason, sizeof(out->reason), "Unsupported dtype");
+    } else {
+        sp24_status st = check_gemm(in_dt, out_dt, M, N, K, {values, meta, dense_other}, Y_scratch,
+                                    scale_x, scale_w, true);
+        if (st == SP24_E_ALIGN) {
+            eligible = 0;
+            snprintf(out->reason, sizeof(out->reason), "Alignment failure");
+        } else if (st != SP24_OK) {
+            return st;
+        }
+    }
+    const void* X = which == SP24_SPARSE_W ? dense_other : dense_pruned;
+    const void* W = which == SP24_SPARSE_W ? dense_pruned : dense_other;
+    sp24_status dst = check_gemm(in_dt, out_dt, M, N, K, {X, W}, Y_scratch, scale_x, scale_w, false);
+    if (dst != SP24_OK)
+        return dst;   // the dense path must run: nothing to fall back to otherwise
+
+    const char* sname = nullptr;
+    const char* dname = nullptr;
+    auto run_sparse = [&](hipEvent_t mid) -> sp24_status {
+        if (which == SP24_SPARSE_X) {
+            sp24_status st = sp24_prune_compress(in_dt, M, K, dense_pruned, K, const_cast<void*>(values),
+                                                 const_cast<uint32_t*>(meta), stream);
+            if (st != SP24_OK)
+                return st;
+        }
+        if (mid && hipEventRecord(mid, stream) != hipSuccess)
+            return SP24_E_HIP;
+        return gemm_impl(which, in_dt, out_dt, M, N, K, values, meta, dense_other, scale_x, scale_w,
+                         Y_scratch, stream, &sname);
+    };
+    auto run_dense = [&]() -> sp24_status {
+        return dense_impl(in_dt, out_dt, M, N, K, X, W, scale_x, scale_w, Y_scratch, stream, &dname);
+    };
+
+    std::vector<hipEvent_t> ev((size_t)reps * 5, nullptr);
+    sp24_status result = SP24_OK;
+    for (auto& e : ev)
+        if (hipEventCreate(&e) != hipSuccess) {
+            result = SP24_E_HIP;
+            break;
+        }
+    std::vector<double> ts, tc, tg, td;
+    if (result == SP24_OK) {
+        for (int i = 0; i < warmup && result == SP24_OK; ++i) {
+            if (eligible)
+                result = run_sparse(nullptr);
+            if (result == SP24_OK)
+                result = run_dense();
+        }
+        // interleave the two paths rep by rep so that clock and thermal drift hit both
+        for (int i = 0; i < reps && result == SP24_OK; ++i) {
+            hipEvent_t* e = &ev[(size_t)i * 5];
+            if (eligible) {
+                if (hipEventRecord(e[0], stream) != hipSuccess) { result = SP24_E_HIP; break; }
+                result = run_sparse(e[1]);
+                if (result != SP24_OK) break;
+                if (hipEventRecord(e[2], stream) != hipSuccess) { result = SP24_E_HIP; break; }
+            }
+            if (hipEventRecord(e[3], stream) != hipSuccess) { result = SP24_E_HIP; break; }
+            result = run_dense();
+            if (result != SP24_OK) break;
+            if (hipEventRecord(e[4], stream) != hipSuccess) { result = SP24_E_HIP; break; }
+        }
+        if (result == SP24_OK && hipStreamSynchronize(stream) != hipSuccess)
+            result = SP24_E_HIP;
+        for (int i = 0; i < reps && result == SP24_OK; ++i) {
+            hipEvent_t* e = &ev[(size_t)i * 5];
+            float a = 0.f, b = 0.f, c = 0.f;
+            if (eligible) {
+                if (hipEventElapsedTime(&a, e[0], e[1]) != hipSuccess ||
+                    hipEventElapsedTime(&b, e[1], e[2]) != hipSuccess) {
+                    result = SP24_E_HIP;
+                    break;
+                }
+                tc.push_back(1e3 * a);
+                tg.push_back(1e3 * b);
+                ts.push_back(1e3 * (a + b));
+            }
+            if (hipEventElapsedTime(&c, e[3], e[4]) != hipSuccess) {
+                result = SP24_E_HIP;
+                break;
+            }
+            td.push_back(1e3 * c);
+        }
+    }
+    for (auto& e : ev)
+        if (e)
+            (void)hipEventDestroy(e);
+    if (result != SP24_OK)
+        return result;
+    char reason[96];
+    memcpy(reason, out->reason, sizeof(reason));
+    result = sp24_tactic_decide(eligible, ts.data(), (int)ts.size(), td.data(), (int)td.size(), out);
+    if (result != SP24_OK)
+        return result;
+    if (!eligible)
+        memcpy(out->reason, reason, sizeof(reason));
+    if (eligible && which == SP24_SPARSE_X) {
+        out->t_compress_us = median(tc);
+        out->t_sparse_us = median(tg);
+    }
+    const char* chosen = out->selected ? sname : dname;
+    snprintf(out->kernel, sizeof(out->kernel), "%s", chosen ? chosen : "none");
+    return SP24_OK;
+}

@@ -1,0 +1,135 @@
+// mfma_ops.h -- thin wrappers over the gfx950 sparse and dense matrix
+// instructions, with the operand layouts measured on the hardware.
+//
+// Sparse (the paper's section 2 "Sparse tensor cores": the compressed first
+// operand A carries two kept values and a 2-bit position per group of four;
+// the positions select the matching elements of the dense operand B):
+//
+//   v_smfmac_f32_16x16x64_{bf16,f16}   (one "step" = 64 dense K)
+//     A, lane l: row l%16; 8 compressed values = the 4 groups of dense K
+//        [16*(l/16), +16), values 2j and 2j+1 belonging to group j;
+//     index: 16 bits per lane, slot s reading bits [2s, 2s+1] -- that is,
+//        group j's nibble p0 | p1 << 2 at bits [4j, 4j+3]; `abid` picks the
+//        low (0) or high (1) half of the 32-bit index register;
+//     B, lane l: column l%16; 16 values = dense K [8*(l/16), +8) followed by
+//        dense K [32 + 8*(l/16), +8);
+//     D, lane l: D[4*(l/16) + i][l%16], i = 0..3.
+//   v_smfmac_f32_16x16x128_fp8_fp8      (one step = 128 dense K)
+//     A, lane l: row l%16; 16 compressed bytes = the 8 groups of dense K
+//        [32*(l/16), +32); index: all 32 bits, group j's nibble at [4j, 4j+3];
+//     B, lane l: column l%16; 32 bytes = dense K [16*(l/16), +16) then
+//        [64 + 16*(l/16), +16);
+//     D as above.
+// With the metadata format of this library (nibble per group, 8 groups per
+// little-endian uint32), lane group kg of a 16-bit step needs the half
+// (kg & 1) of word (2*step + kg/2) of its row: one shift per lane.  An fp8
+// step's lane group kg needs word (4*step + kg) unchanged.
+//
+// Dense:
+//   v_mfma_f32_32x32x16_{bf16,f16}: A/B lane l: row/column l%32, dense K
+//     [8*(l/32), +8); D lane l: D[8*(i/4) + 4*(l/32) + i%4][l%32], i=0..15.
+//   v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 both sides, unit E8M0 scales):
+//     A/B lane l: row/column l%32, 32 bytes of dense K [32*(l/32), +32).
+#pragma once
+
+#include "sp24_internal.h"
+
+namespace sp24 {
+
+template <sp24_dtype DT>
+struct SparseOp;
+
+template <>
+struct SparseOp<SP24_BF16> {
+    static constexpr int KSTEP = 64;        // dense K per instruction
+    static constexpr int ELEM = 2;          // bytes per element
+    __device__ static __forceinline__ f32x4 mma(uint4 a, uint4 b0, uint4 b1, uint32_t idx, f32x4 c) {
+        bf16x8 av = __builtin_bit_cast(bf16x8, a);
+        struct { uint4 x, y; } bb = {b0, b1};
+        bf16x16 bv = __builtin_bit_cast(bf16x16, bb);
+        return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(av, bv, c, (int)idx, 0, 0);
+    }
+};
+
+template <>
+struct SparseOp<SP24_F16> {
+    static constexpr int KSTEP = 64;
+    static constexpr int ELEM = 2;
+    __device__ static __forceinline__ f32x4 mma(uint4 a, uint4 b0, uint4 b1, uint32_t idx, f32x4 c) {
+        f16x8 av = __builtin_bit_cast(f16x8, a);
+        struct { uint4 x, y; } bb = {b0, b1};
+        f16x16 bv = __builtin_bit_cast(f16x16, bb);
+        return __builtin_amdgcn_smfmac_f32_16x16x64_f16(av, bv, c, (int)idx, 0, 0);
+    }
+};
+
+template <>
+struct SparseOp<SP24_E4M3> {
+    static constexpr int KSTEP = 128;
+    static constexpr int ELEM = 1;
+    __device__ static __forceinline__ f32x4 mma(uint4 a, uint4 b0, uint4 b1, uint32_t idx, f32x4 c) {
+        i32x4 av = __builtin_bit_cast(i32x4, a);
+        struct { uint4 x, y; } bb = {b0, b1};
+        i32x8 bv = __builtin_bit_cast(i32x8, bb);
+        return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(av, bv, c, (int)idx, 0, 0);
+    }
+};
+
+// Byte offsets, within one step of one row, of what lane group kg loads.
+//   A values: 16 bytes at a_off(kg) of the row's compressed step (KSTEP/2 values)
+//   B: 16 bytes at b_off0(kg) and 16 at b_off1(kg) of the row's dense step
+template <sp24_dtype DT>
+struct StepLayout {
+    static constexpr int KSTEP = SparseOp<DT>::KSTEP;
+    static constexpr int ELEM = SparseOp<DT>::ELEM;
+    static constexpr int A_STEP_BYTES = KSTEP / 2 * ELEM;     // 64 B
+    static constexpr int B_STEP_BYTES = KSTEP * ELEM;         // 128 B
+    static constexpr int META_WORDS = KSTEP / 32;             // 2 or 4 words per step
+    __device__ static __forceinline__ int a_off(int kg) { return 16 * kg; }
+    __device__ static __forceinline__ int b_off0(int kg) { return 16 * kg; }
+    __device__ static __forceinline__ int b_off1(int kg) { return B_STEP_BYTES / 2 + 16 * kg; }
+    // metadata word of this step used by lane group kg, and the shift to
+    // bring its 16 (or 32) bits to the bottom
+    __device__ static __forceinline__ int meta_word(int kg) { return ELEM == 2 ? kg >> 1 : kg; }
+    __device__ static __forceinline__ int meta_shift(int kg) { return ELEM == 2 ? 16 * (kg & 1) : 0; }
+};
+
+// fp32 -> output element, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);     // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+    _Float16 h = (_Float16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+template <sp24_dtype OUT>
+__device__ __forceinline__ void store_out(void* Y, int64_t off, float v) {
+    if constexpr (OUT == SP24_F32)
+        reinterpret_cast<float*>(Y)[off] = v;
+    else if constexpr (OUT == SP24_BF16)
+        reinterpret_cast<uint16_t*>(Y)[off] = f32_to_bf16_rne(v);
+    else
+        reinterpret_cast<uint16_t*>(Y)[off] = f32_to_f16_rne(v);
+}
+
+// Four consecutive outputs (offset off .. off+3), vectorized when aligned.
+template <sp24_dtype OUT>
+__device__ __forceinline__ void store_out4(void* Y, int64_t off, f32x4 v) {
+    if constexpr (OUT == SP24_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(Y) + off) = v;
+    } else {
+        uint16_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            h[i] = OUT == SP24_BF16 ? f32_to_bf16_rne(v[i]) : f32_to_f16_rne(v[i]);
+        uint2 p = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) = p;
+    }
+}
+
+}  // namespace sp24

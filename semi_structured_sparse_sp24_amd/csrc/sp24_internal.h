@@ -1,0 +1,62 @@
+// sp24_internal.h -- declarations shared by the HIP kernels and the C-ABI
+// glue of libsp24.so.  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sp24.h"
+
+namespace sp24 {
+
+// ------------------------------------------------------------------ types
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) __bf16 bf16x16;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(16))) _Float16 f16x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+inline int elem_bytes(sp24_dtype dt) { return dt == SP24_E4M3 ? 1 : (dt == SP24_F32 ? 4 : 2); }
+inline int64_t meta_words(int64_t K) { return (K + 31) / 32; }
+
+// K consumed by one sparse MFMA step, per input dtype: 64 for 16-bit
+// (v_smfmac_*_16x16x64), 128 for fp8 (v_smfmac_*_16x16x128).
+inline int64_t gemm_k_tile(sp24_dtype dt) { return dt == SP24_E4M3 ? 128 : 64; }
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error; arguments were validated by
+// the caller.
+hipError_t launch_prune_compress(sp24_dtype dt, int64_t rows, int64_t K, const void* src,
+                                 int64_t ld_src, void* values, uint32_t* meta, hipStream_t s);
+hipError_t launch_decompress(sp24_dtype dt, int64_t rows, int64_t K, const void* values,
+                             const uint32_t* meta, void* dst, int64_t ld_dst, hipStream_t s);
+
+struct GemmArgs {
+    sp24_dtype in_dt, out_dt;
+    int64_t M, N, K;
+    const void* a_vals;      // compressed operand values (rows x K/2)
+    const uint32_t* a_meta;  // its metadata (rows x K/32)
+    const void* b;           // dense operand (cols x K)
+    const float* scale_a;    // per compressed-operand row, or null
+    const float* scale_b;    // per dense-operand row, or null
+    void* Y;                 // M x N
+    int a_is_w;              // 1: compressed operand is W (rows = N), 0: it is X (rows = M)
+};
+// Sparse GEMM; writes the name of the kernel it launched into kname (if non-null).
+hipError_t launch_sp24_gemm(const GemmArgs& g, hipStream_t s, const char** kname);
+
+struct DenseArgs {
+    sp24_dtype in_dt, out_dt;
+    int64_t M, N, K;
+    const void* X;
+    const void* W;
+    const float* scale_x;
+    const float* scale_w;
+    void* Y;
+};
+hipError_t launch_dense_gemm(const DenseArgs& g, hipStream_t s, const char** kname);
+
+}  // namespace sp24

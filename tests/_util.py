@@ -1,0 +1,43 @@
+"""Helpers shared by the GPU tests: moving bit patterns between numpy and the
+device, and the GEMM tolerance."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+TORCH_OF = {oracle.F16: torch.float16, oracle.BF16: torch.bfloat16, oracle.E4M3: torch.float8_e4m3fn,
+            oracle.F32: torch.float32}
+VIEW_OF = {oracle.F16: torch.int16, oracle.BF16: torch.int16, oracle.E4M3: torch.uint8, oracle.F32: torch.int32}
+NP_OF = {oracle.F16: np.uint16, oracle.BF16: np.uint16, oracle.E4M3: np.uint8, oracle.F32: np.uint32}
+
+# Parity bar for GEMM outputs: max |Y - R| / max(|R|, rms R).  fp16/bf16 inputs
+# with fp32 accumulation: 1e-2; fp8 e4m3: 3e-2 (both sides on the same
+# e4m3-decoded values).  The error the arithmetic itself allows is far lower:
+# one output rounding (bf16: 2^-9 relative) plus fp32 accumulation
+# (~sqrt(K) * 2^-24 relative to sum |x w|).
+TOL = {oracle.F16: 1e-2, oracle.BF16: 1e-2, oracle.E4M3: 3e-2}
+
+
+def say(*msg):
+    print("[case]", *msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits: np.ndarray, dt: int) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(NP_OF[dt]).view(
+        {np.uint16: np.int16, np.uint8: np.uint8, np.uint32: np.int32}[NP_OF[dt]]))
+    return t.view(VIEW_OF[dt]).view(TORCH_OF[dt]).cuda()
+
+
+def to_host(t: torch.Tensor, dt: int) -> np.ndarray:
+    return t.detach().contiguous().cpu().view(VIEW_OF[dt]).numpy().view(NP_OF[dt])
+
+
+def meta_host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().numpy().view(np.uint32)
+
+
+def decode_out(Y: torch.Tensor) -> np.ndarray:
+    return Y.detach().float().cpu().numpy().astype(np.float64)

@@ -1,0 +1,135 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, rejects bad arguments before any HIP call, and applies the
+tactic decision rule to injected timings.  No GPU is touched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import semi_structured_sparse_sp24_amd as sp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sp24.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("sp24_prune_compress", "sp24_decompress", "sp24_gemm", "dense_gemm",
+                     "sp24_select_tactic", "sp24_tactic_decide", "sp24_status_str"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sp.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(sp.SIGNATURES) == set(_declared_functions())
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in sp.version()
+    for code in range(6):
+        s = sp.lib().sp24_status_str(code).decode()
+        assert s.startswith(sp.STATUS[code])
+    assert sp.meta_words_per_row(100) == 4 and sp.meta_words_per_row(0) == 0
+
+
+def _pc(dt=sp.BF16, rows=4, K=64, src=16, ld=None, vals=32, meta=48):
+    return sp.lib().sp24_prune_compress(dt, rows, K, src, K if ld is None else ld, vals, meta, None)
+
+
+def test_prune_compress_validation_precedes_hip():
+    assert _pc(dt=sp.F32) == 3                    # fp32 is an output dtype only
+    assert _pc(dt=7) == 3
+    assert _pc(K=6) == 2                          # K % 4
+    assert _pc(rows=-1) == 2
+    assert _pc(ld=32) == 2                        # ld < K
+    assert _pc(src=None) == 1
+    assert _pc(meta=None) == 1
+    assert _pc(rows=0) == 0 and _pc(K=0) == 0     # empty: no-op, nothing launched
+
+
+def _gemm(which=sp.SPARSE_W, in_dt=sp.BF16, out_dt=sp.BF16, M=4, N=16, K=128, v=16, m=32, d=48,
+          sx=None, sw=None, y=64):
+    return sp.lib().sp24_gemm(which, in_dt, out_dt, M, N, K, v, m, d, sx, sw, y, None)
+
+
+def test_gemm_validation_precedes_hip():
+    assert _gemm(which=3) == 2
+    assert _gemm(in_dt=sp.F32) == 3
+    assert _gemm(in_dt=sp.E4M3, out_dt=sp.F16) == 3
+    assert _gemm(K=6) == 2
+    assert _gemm(M=-1) == 2
+    assert _gemm(v=None) == 1
+    assert _gemm(y=None) == 1
+    assert _gemm(K=96) == 4                       # not a multiple of the 64-K step: ineligible
+    assert _gemm(in_dt=sp.E4M3, K=192) == 4       # fp8 step is 128
+    assert _gemm(d=40) == 4                       # misaligned dense operand
+    assert _gemm(y=72) == 4
+    assert _gemm(sx=66) == 4                      # misaligned scale vector
+    assert _gemm(M=0) == 0 and _gemm(N=0) == 0    # empty output: no-op
+    assert sp.lib().dense_gemm(sp.BF16, sp.BF16, 4, 16, 100, 16, 32, None, None, 48, None) == 4
+    assert sp.lib().dense_gemm(sp.BF16, sp.BF16, 4, 16, 128, None, 32, None, None, 48, None) == 1
+
+
+def test_decompress_validation_precedes_hip():
+    f = sp.lib().sp24_decompress
+    assert f(sp.F32, 4, 64, 16, 32, 48, 64, None) == 3
+    assert f(sp.BF16, 4, 66, 16, 32, 48, 66, None) == 2
+    assert f(sp.BF16, 4, 64, 16, 32, 48, 60, None) == 2
+    assert f(sp.BF16, 4, 64, None, 32, 48, 64, None) == 1
+
+
+def test_select_tactic_validation():
+    rec = sp.Tactic()
+    f = sp.lib().sp24_select_tactic
+    assert f(0, sp.BF16, sp.BF16, 4, 16, 128, 16, 32, 48, 64, None, None, 80, 1, 0, None, ctypes.byref(rec)) == 2
+    assert f(0, sp.BF16, sp.BF16, 4, 16, 128, 16, 32, 48, 64, None, None, 80, 1, 5, None, None) == 1
+    # the dense path must be runnable: a null dense operand is an error, not a fallback
+    assert f(0, sp.BF16, sp.BF16, 4, 16, 128, 16, 32, 48, None, None, None, 80, 1, 5, None,
+             ctypes.byref(rec)) == 1
+
+
+# ------------------------------------------------------------ decision rule
+
+def test_decide_sparse_strictly_faster():
+    r = sp.tactic_decide(True, [10.0, 9.0, 11.0], [12.0, 13.0, 12.5])
+    assert r["selected"] == "sparse" and r["t_sparse_us"] == 10.0 and r["t_dense_us"] == 12.5
+    assert r["ratio"] == pytest.approx(1.25)
+    assert r["reason"] == "Sparse kernel 1.25x faster"
+
+
+def test_decide_dense_faster_reports_margin():
+    r = sp.tactic_decide(True, [11.5, 11.5], [10.0, 10.0])
+    assert r["selected"] == "dense"
+    assert r["reason"] == "Dense kernel 1.15x faster"        # the form of the pages' manifest example
+
+
+def test_decide_tie_keeps_dense():
+    r = sp.tactic_decide(True, [5.0, 6.0, 7.0], [6.0, 6.0, 6.0])
+    assert r["selected"] == "dense" and "Tie" in r["reason"]
+
+
+def test_decide_uses_medians_not_means():
+    # one outlier rep must not flip the choice
+    r = sp.tactic_decide(True, [8.0, 8.0, 8.0, 8.0, 1000.0], [9.0, 9.0, 9.0, 9.0, 9.0])
+    assert r["selected"] == "sparse"
+
+
+def test_decide_ineligible_is_dense():
+    r = sp.tactic_decide(False, [], [3.0])
+    assert r["selected"] == "dense" and not r["eligible"]
+
+
+def test_decide_rejects_missing_timings():
+    with pytest.raises(sp.Sp24Error):
+        sp.tactic_decide(True, [], [1.0])
+    with pytest.raises(sp.Sp24Error):
+        sp.tactic_decide(True, [1.0], [])

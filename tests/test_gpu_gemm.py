@@ -1,0 +1,306 @@
+"""GPU parity of the sparse GEMM (weight- and activation-sparse) and the
+dense GEMM against the oracle's fp64 product on the decompressed operand:
+
+  - small shapes spanning several tiles with ragged tails, both kernel
+    families (skinny M <= 64 and tiled), every dtype and output type;
+  - exact-integer inputs, where fp32 accumulation is exact and the GPU output
+    must equal the oracle bit for bit;
+  - every workload at full size in the launch configuration the bench uses,
+    checked on sampled rows of M;
+  - edge cases: empty outputs, K = 0, ineligible K, guard bands, reruns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import semi_structured_sparse_sp24_amd as sp
+from semi_structured_sparse_sp24_amd import inputs
+from tests._util import TOL, decode_out, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+OUT_T = {oracle.F16: torch.float16, oracle.BF16: torch.bfloat16, oracle.F32: torch.float32}
+
+
+def _operands(dt, M, N, K, seed, integer=False):
+    if integer:
+        xb = inputs.integer_operand((M, K), seed, dt)
+        wb = inputs.integer_operand((N, K), seed + 1, dt)
+        return xb, None, wb, None
+    x = inputs.normal((M, K), 1.0, seed)
+    w = inputs.normal((N, K), 0.02, seed + 1)
+    if dt == oracle.E4M3:
+        xb, sx = inputs.quantize_e4m3_rows(x)
+        wb, sw = inputs.quantize_e4m3_rows(w)
+        return xb, sx, wb, sw
+    return inputs.to_bits(x, dt), None, inputs.to_bits(w, dt), None
+
+
+def _sparse_w(dt, out, M, N, K, seed=1, integer=False, mrows=None):
+    xb, sx, wb, sw = _operands(dt, M, N, K, seed, integer)
+    wv, wm = oracle.prune_compress(dt, wb)
+    R = oracle.gemm(dt, M, N, K, x=xb, w_vals=wv, w_meta=wm, scale_x=sx, scale_w=sw, mrows=mrows)
+    W = to_dev(wb, dt)
+    X = to_dev(xb, dt)
+    v, m = sp.prune_compress(W)
+    dsx = None if sx is None else torch.from_numpy(sx).cuda()
+    dsw = None if sw is None else torch.from_numpy(sw).cuda()
+    Y = sp.sp24_gemm(sp.SPARSE_W, v, m, X, M, N, K, out_dtype=OUT_T[out], scale_x=dsx, scale_w=dsw)
+    torch.cuda.synchronize()
+    Yh = decode_out(Y)
+    return (Yh if mrows is None else Yh[mrows]), R, Y
+
+
+def _sparse_x(dt, out, M, N, K, seed=1, integer=False):
+    xb, sx, wb, sw = _operands(dt, M, N, K, seed, integer)
+    xv, xm = oracle.prune_compress(dt, xb)
+    R = oracle.gemm(dt, M, N, K, x_vals=xv, x_meta=xm, w=wb, scale_x=sx, scale_w=sw)
+    v, m = sp.prune_compress(to_dev(xb, dt))
+    dsx = None if sx is None else torch.from_numpy(sx).cuda()
+    dsw = None if sw is None else torch.from_numpy(sw).cuda()
+    Y = sp.sp24_gemm(sp.SPARSE_X, v, m, to_dev(wb, dt), M, N, K, out_dtype=OUT_T[out],
+                     scale_x=dsx, scale_w=dsw)
+    torch.cuda.synchronize()
+    return decode_out(Y), R, Y
+
+
+def _dense(dt, out, M, N, K, seed=1, integer=False, prune_w=True):
+    xb, sx, wb, sw = _operands(dt, M, N, K, seed, integer)
+    if prune_w:
+        wb = oracle.prune(dt, wb)
+    R = oracle.gemm(dt, M, N, K, x=xb, w=wb, scale_x=sx, scale_w=sw)
+    dsx = None if sx is None else torch.from_numpy(sx).cuda()
+    dsw = None if sw is None else torch.from_numpy(sw).cuda()
+    Y = sp.dense_gemm(to_dev(xb, dt), to_dev(wb, dt), out_dtype=OUT_T[out], scale_x=dsx, scale_w=dsw)
+    torch.cuda.synchronize()
+    return decode_out(Y), R, Y
+
+
+DT_OUT = [(oracle.BF16, oracle.BF16), (oracle.F16, oracle.F16), (oracle.BF16, oracle.F32),
+          (oracle.F16, oracle.BF16), (oracle.E4M3, oracle.BF16), (oracle.E4M3, oracle.F32)]
+SMALL = [(1, 16, 256), (4, 48, 256), (16, 130, 512), (17, 33, 256), (63, 64, 384), (64, 200, 256),
+         (65, 130, 256), (200, 96, 512), (300, 260, 1024)]
+
+
+def _k(dt, K):
+    return K if dt != oracle.E4M3 else max(128, K // 128 * 128)
+
+
+@pytest.mark.parametrize("dt,out", DT_OUT)
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_sparse_w_small(dt, out, M, N, K):
+    K = _k(dt, K)
+    say("sparse_w", dt, out, M, N, K)
+    Y, R, _ = _sparse_w(dt, out, M, N, K, seed=M * 31 + N)
+    assert oracle.relative_error(Y, R) <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt,out", DT_OUT)
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_sparse_x_small(dt, out, M, N, K):
+    K = _k(dt, K)
+    say("sparse_x", dt, out, M, N, K)
+    Y, R, _ = _sparse_x(dt, out, M, N, K, seed=M * 37 + N)
+    assert oracle.relative_error(Y, R) <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt,out", DT_OUT)
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_dense_small(dt, out, M, N, K):
+    K = _k(dt, K)
+    say("dense", dt, out, M, N, K)
+    Y, R, _ = _dense(dt, out, M, N, K, seed=M * 41 + N)
+    assert oracle.relative_error(Y, R) <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 1024), (16, 48, 2048), (64, 128, 512), (130, 200, 1024),
+                                   (256, 256, 2048)])
+def test_exact_integer_bitwise(dt, M, N, K):
+    """|sums| < 2^24: fp32 accumulation is exact in any order, so f32 output
+    equals the oracle exactly and 16-bit output equals its RNE encoding."""
+    K = _k(dt, K)
+    say("exact", dt, M, N, K)
+    Y, R, _ = _sparse_w(dt, oracle.F32, M, N, K, seed=M + N, integer=True)
+    assert np.array_equal(Y, R)
+    Y, R, _ = _sparse_x(dt, oracle.F32, M, N, K, seed=M + N + 5, integer=True)
+    assert np.array_equal(Y, R)
+    Y, R, _ = _dense(dt, oracle.F32, M, N, K, seed=M + N + 9, integer=True)
+    assert np.array_equal(Y, R)
+    Y, R, Yd = _sparse_w(dt, oracle.BF16, M, N, K, seed=M + N + 13, integer=True)
+    assert np.array_equal(to_host(Yd, oracle.BF16), oracle.encode(oracle.BF16, R))
+    if dt != oracle.E4M3:
+        Y, R, Yd = _sparse_x(dt, oracle.F16, M, N, K, seed=M + N + 17, integer=True)
+        assert np.array_equal(to_host(Yd, oracle.F16), oracle.encode(oracle.F16, R))
+
+
+def test_one_hot_rows_read_back_weights():
+    """X = identity rows: Y[m, :] is column m of the decompressed W, which
+    checks every metadata position and word through the sparse MMA."""
+    dt, K, N = oracle.BF16, 256, 96
+    wb = inputs.to_bits(inputs.normal((N, K), 1.0, 3), dt)
+    v, m = sp.prune_compress(to_dev(wb, dt))
+    for M0 in (0, 64):           # skinny (M = 64) and tiled (M = 128) kernels
+        M = 64 if M0 == 0 else 128
+        eye = torch.zeros((M, K), dtype=torch.float32)
+        for i in range(M):
+            eye[i, (i + M0) % K] = 1.0
+        X = to_dev(inputs.to_bits(eye, dt), dt)
+        Y = sp.sp24_gemm(sp.SPARSE_W, v, m, X, M, N, K, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        wp = oracle.decode(dt, oracle.prune(dt, wb))
+        cols = [(i + M0) % K for i in range(M)]
+        assert np.array_equal(decode_out(Y), wp[:, cols].T)
+
+
+# ------------------------------------------------------------------ full size
+
+def _sample_rows(M):
+    rows = sorted({0, M - 1, M // 2, (M * 7) // 11})
+    return np.array([r for r in rows if 0 <= r < M], dtype=np.int64)
+
+
+FULL = []
+for wl in ("tiny", "decode", "prefill", "fp8"):
+    w = inputs.WORKLOADS[wl]
+    for s in range(len(w["shapes"])):
+        for j in range(len(w["ms"])):
+            FULL.append((wl, s, j))
+
+
+@pytest.mark.parametrize("wl,s,j", FULL)
+def test_full_size_sparse_and_dense(wl, s, j):
+    w = inputs.WORKLOADS[wl]
+    dt, out = w["dtype"], w["out"]
+    N, K = w["shapes"][s]
+    M = w["ms"][j]
+    say("full", wl, (N, K), "M", M)
+    wb, sw = inputs.weight(wl, s)
+    xb, sx = inputs.activation(wl, s, j)
+    wv, wm = oracle.prune_compress(dt, wb)
+    rows = np.arange(M) if M <= 16 else _sample_rows(M)
+    R = oracle.gemm(dt, M, N, K, x=xb, w_vals=wv, w_meta=wm, scale_x=sx, scale_w=sw, mrows=rows)
+    W = to_dev(wb, dt)
+    X = to_dev(xb, dt)
+    dsx = None if sx is None else torch.from_numpy(sx).cuda()
+    dsw = None if sw is None else torch.from_numpy(sw).cuda()
+    v, m = sp.prune_compress(W)
+    Y = sp.sp24_gemm(sp.SPARSE_W, v, m, X, M, N, K, out_dtype=OUT_T[out], scale_x=dsx, scale_w=dsw)
+    Wp = sp.decompress(v, m, K)
+    Yd = sp.dense_gemm(X, Wp, out_dtype=OUT_T[out], scale_x=dsx, scale_w=dsw)
+    torch.cuda.synchronize()
+    rt = torch.from_numpy(rows).cuda()
+    e_s = oracle.relative_error(decode_out(Y[rt]), R)
+    e_d = oracle.relative_error(decode_out(Yd[rt]), R)
+    say("  rel err sparse", e_s, "dense", e_d)
+    assert e_s <= TOL[dt] and e_d <= TOL[dt]
+    # every output, not only the sampled rows, is finite
+    assert bool(torch.isfinite(Y.float()).all()) and bool(torch.isfinite(Yd.float()).all())
+
+
+def test_full_size_online_activation():
+    dt = oracle.BF16
+    M, N, K = 4096, 4096, 4096
+    say("full online", M, N, K)
+    xb, _ = inputs.activation("online", 0, 0)
+    wb, _ = inputs.weight("online", 0)
+    xv, xm = oracle.prune_compress(dt, xb)
+    rows = _sample_rows(M)
+    R = oracle.gemm(dt, M, N, K, x_vals=xv, x_meta=xm, w=wb, mrows=rows)
+    X = to_dev(xb, dt)
+    W = to_dev(wb, dt)
+    v, m = sp.prune_compress(X)
+    Y = sp.sp24_gemm(sp.SPARSE_X, v, m, W, M, N, K)
+    Yd = sp.dense_gemm(X, W)
+    torch.cuda.synchronize()
+    rt = torch.from_numpy(rows).cuda()
+    assert oracle.relative_error(decode_out(Y[rt]), R) <= TOL[dt]
+    Rd = oracle.gemm(dt, M, N, K, x=xb, w=wb, mrows=rows)
+    assert oracle.relative_error(decode_out(Yd[rt]), Rd) <= TOL[dt]
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_empty_and_zero_k():
+    X = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((32, 128), dtype=torch.bfloat16, device="cuda")
+    v, m = sp.prune_compress(W)
+    assert sp.sp24_gemm(sp.SPARSE_W, v, m, X, 0, 32, 128).shape == (0, 32)
+    assert sp.dense_gemm(X, W).shape == (0, 32)
+    # K = 0: the empty sum, Y = 0
+    X0 = torch.zeros((5, 0), dtype=torch.bfloat16, device="cuda")
+    W0 = torch.zeros((7, 0), dtype=torch.bfloat16, device="cuda")
+    v0, m0 = sp.prune_compress(W0)
+    Y = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device="cuda")
+    sp.sp24_gemm(sp.SPARSE_W, v0, m0, X0, 5, 7, 0, out=Y)
+    torch.cuda.synchronize()
+    assert bool((Y == 0).all())
+
+
+def test_ineligible_shapes_raise_align():
+    X = torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((32, 96), dtype=torch.bfloat16, device="cuda")
+    v, m = sp.prune_compress(W)
+    with pytest.raises(sp.Sp24Error) as e:
+        sp.sp24_gemm(sp.SPARSE_W, v, m, X, 4, 32, 96)
+    assert e.value.status == 4
+
+
+def test_output_guard_bands():
+    dt = oracle.BF16
+    for M, N, K in ((5, 40, 256), (130, 72, 256)):
+        say("guard", M, N, K)
+        xb, _, wb, _ = _operands(dt, M, N, K, 99)
+        guard = 512
+        buf = torch.full((M * N + 2 * guard,), 0x7A7A, dtype=torch.int16, device="cuda")
+        Y = buf[guard:guard + M * N].view(torch.bfloat16).view(M, N)
+        v, m = sp.prune_compress(to_dev(wb, dt))
+        sp.sp24_gemm(sp.SPARSE_W, v, m, to_dev(xb, dt), M, N, K, out=Y)
+        torch.cuda.synchronize()
+        b = buf.cpu().numpy()
+        assert np.all(b[:guard] == 0x7A7A) and np.all(b[-guard:] == 0x7A7A)
+        Yx = buf[guard:guard + M * N].view(torch.bfloat16).view(M, N)
+        sp.dense_gemm(to_dev(xb, dt), to_dev(wb, dt), out=Yx)
+        torch.cuda.synchronize()
+        b = buf.cpu().numpy()
+        assert np.all(b[:guard] == 0x7A7A) and np.all(b[-guard:] == 0x7A7A)
+
+
+def test_reruns_are_bitwise_stable():
+    for M in (16, 512):
+        xb, _, wb, _ = _operands(oracle.BF16, M, 1024, 2048, 7)
+        X, W = to_dev(xb, oracle.BF16), to_dev(wb, oracle.BF16)
+        v, m = sp.prune_compress(W)
+        a = sp.sp24_gemm(sp.SPARSE_W, v, m, X, M, 1024, 2048)
+        b = sp.sp24_gemm(sp.SPARSE_W, v, m, X, M, 1024, 2048)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_select_tactic_record():
+    dt = oracle.BF16
+    for (M, N, K, which) in ((16, 4096, 4096, sp.SPARSE_W), (512, 4096, 4096, sp.SPARSE_W),
+                             (1024, 1024, 1024, sp.SPARSE_X)):
+        say("tactic", M, N, K, which)
+        xb, _, wb, _ = _operands(dt, M, N, K, 5)
+        X, W = to_dev(xb, dt), to_dev(wb, dt)
+        if which == sp.SPARSE_W:
+            v, m = sp.prune_compress(W)
+            rec = sp.select_tactic(which, v, m, X, sp.decompress(v, m, K), M, N, K, reps=10)
+        else:
+            v = torch.empty((M, K // 2), dtype=torch.bfloat16, device="cuda")
+            m = torch.empty((M, K // 32), dtype=torch.int32, device="cuda")
+            rec = sp.select_tactic(which, v, m, W, X, M, N, K, reps=10)
+            assert rec["t_compress_us"] > 0
+        say("  ", rec)
+        assert rec["eligible"]
+        assert (rec["selected"] == "sparse") == (rec["ratio"] > 1.0)
+        assert rec["t_sparse_us"] > 0 and rec["t_dense_us"] > 0
+        assert rec["kernel"].startswith("sp24_" if rec["selected"] == "sparse" else "dense_")
+    # ineligible shape: dense with the alignment reason
+    X = torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((32, 96), dtype=torch.bfloat16, device="cuda")
+    v, m = sp.prune_compress(W)
+    rec = sp.select_tactic(sp.SPARSE_W, v, m, X, W, 4, 32, 96, reps=3)
+    assert not rec["eligible"] and rec["selected"] == "dense" and rec["reason"] == "Alignment failure"
