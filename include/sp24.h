@@ -75,7 +75,8 @@ typedef enum {
 typedef enum {
     SP24_OK = 0,
     SP24_E_NULL = 1,     /* a required pointer is NULL */
-    SP24_E_SHAPE = 2,    /* a size is negative, K % 4 != 0, or a leading dimension < K */
+    SP24_E_SHAPE = 2,    /* a size is negative, K % 4 != 0, a leading dimension < K, or a GEMM
+                            operand (plus 256 rows) of 2 GiB or more */
     SP24_E_DTYPE = 3,    /* unsupported dtype or dtype combination */
     SP24_E_ALIGN = 4,    /* pointer not 16-byte aligned, or K not a multiple of the GEMM's K tile */
     SP24_E_HIP = 5       /* the HIP runtime reported an error (launch, event, device query) */

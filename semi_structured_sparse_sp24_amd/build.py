@@ -15,13 +15,16 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsp24.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "compress.hip", "gemm_sparse.hip", "gemm_dense.hip"]
+SOURCES = ["api.hip", "compress.hip", "gemm_sparse.hip", "gemm_sparse_big.hip", "gemm_dense.hip"]
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
     # packed fp32 ops stay off: the compiler must not form v_pk_{add,mul,fma}_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the large GEMM tiles fully unroll loops over 64 accumulator fragments per stage; the default
+    # limit on pragma-requested unrolling would leave them partly rolled (accumulators on the stack)
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 

@@ -49,6 +49,12 @@ sp24_status check_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N
         return SP24_E_SHAPE;
     if (M > INT32_MAX / 2 || N > INT32_MAX / 2)
         return SP24_E_SHAPE;
+    // the kernels address each operand with 32-bit buffer offsets, and mark
+    // masked loads by adding 2^31 to an offset that may run up to one tile
+    // (256 rows) past the operand: operand + 256 rows must stay below 2 GiB
+    const int64_t eb = elem_bytes(in_dt), lim = (int64_t)1 << 31;
+    if ((M + 256) * K * eb >= lim || (N + 256) * K * eb >= lim)
+        return SP24_E_SHAPE;
     if (M == 0 || N == 0)
         return SP24_OK;
     if (!Y)

@@ -18,8 +18,6 @@
 namespace sp24 {
 namespace {
 
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
 // 16x16 output, one "step" of dense K: 64 (16-bit) or 128 (fp8).  A lane
 // (row l%16, group kg = l/16) supplies 16 bytes at byte offsets o0(kg) and
 // o1(kg) of the row's step; B likewise.  The instructions only need A and B
@@ -91,13 +89,16 @@ struct DenseOp32<SP24_E4M3> {
 };
 
 // ------------------------------------------------------------------ skinny
-template <sp24_dtype DT, sp24_dtype OUT, int MT, int WAVES, int U>
-__global__ void __launch_bounds__(WAVES * 64)
+constexpr int kMaxWaves = 16;
+
+template <sp24_dtype DT, sp24_dtype OUT, int MT, int U>
+__global__ void __launch_bounds__(kMaxWaves * 64)
 dense_skinny(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
              const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K) {
     using Op = DenseOp16<DT>;
     constexpr int STEP_BYTES = Op::KSTEP * Op::ELEM;   // 128
-    __shared__ float red[WAVES][MT][4][64];
+    __shared__ float red[kMaxWaves][MT][4][64];
+    const int WAVES = blockDim.x >> 6;   // 4, 8 or 16: the waves split K
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, kg = lane >> 4;
     const int n0 = blockIdx.x * 16;
@@ -105,41 +106,46 @@ dense_skinny(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const
     const int64_t row_bytes = K * Op::ELEM;
     const int o0 = 16 * kg, o1 = STEP_BYTES / 2 + 16 * kg;
 
-    const bool a_ok = n0 + r < N;
-    const uint8_t* ap = W + (int64_t)(a_ok ? n0 + r : 0) * row_bytes;
-    const uint8_t* bp[MT];
-    bool b_ok[MT];
+    const Buf bufW(W, (uint32_t)N * (uint32_t)row_bytes);   // rows past N / M read as zeros
+    const Buf bufX(X, (uint32_t)M * (uint32_t)row_bytes);
+    const uint32_t a_base = (uint32_t)(n0 + r) * (uint32_t)row_bytes;
+    uint32_t b_base[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        b_ok[mt] = mt * 16 + r < M;
-        bp[mt] = X + (int64_t)(b_ok[mt] ? mt * 16 + r : 0) * row_bytes;
-    }
+    for (int mt = 0; mt < MT; ++mt)
+        b_base[mt] = (uint32_t)(mt * 16 + r) * (uint32_t)row_bytes;
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
         acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int s0 = wave; s0 < steps; s0 += WAVES * U) {
+    // contiguous K chunk per wave, K loop rotated per workgroup (as in the
+    // sparse kernel)
+    const int chunk = (steps + WAVES - 1) / WAVES;
+    const int rot = (int)((blockIdx.x * 13u) % (unsigned)max(steps, 1));
+    for (int i0 = 0; i0 < chunk; i0 += U) {
         uint4 a0[U], a1[U], b0[U][MT], b1[U][MT];
+        bool live[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s = s0 + u * WAVES;
+            const int sl = wave * chunk + i0 + u;
+            live[u] = i0 + u < chunk && sl < steps;
+            int s = sl + rot;
+            s = s >= steps ? s - steps : s;
             // 16-byte chunks past K (a partial last step) read as zeros
-            const bool in0 = s < steps && (int64_t)s * STEP_BYTES + o0 < row_bytes;
-            const bool in1 = s < steps && (int64_t)s * STEP_BYTES + o1 < row_bytes;
-            const uint8_t* p = ap + (int64_t)s * STEP_BYTES;
-            a0[u] = (in0 && a_ok) ? ld16(p + o0) : zero;
-            a1[u] = (in1 && a_ok) ? ld16(p + o1) : zero;
+            const int64_t k0 = (int64_t)s * STEP_BYTES;
+            const bool in0 = live[u] && k0 + o0 < row_bytes;
+            const bool in1 = live[u] && k0 + o1 < row_bytes;
+            const uint32_t d0 = in0 ? (uint32_t)(k0 + o0) : kOOB, d1 = in1 ? (uint32_t)(k0 + o1) : kOOB;
+            a0[u] = bufW.ld16(a_base + d0);
+            a1[u] = bufW.ld16(a_base + d1);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const uint8_t* q = bp[mt] + (int64_t)s * STEP_BYTES;
-                b0[u][mt] = (in0 && b_ok[mt]) ? ld16(q + o0) : zero;
-                b1[u][mt] = (in1 && b_ok[mt]) ? ld16(q + o1) : zero;
+                b0[u][mt] = bufX.ld16(b_base[mt] + d0);
+                b1[u][mt] = bufX.ld16(b_base[mt] + d1);
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (s0 + u * WAVES < steps)
+            if (live[u])
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     acc[mt] = Op::mma(a0[u], a1[u], b0[u][mt], b1[u][mt], acc[mt]);
@@ -154,8 +160,7 @@ dense_skinny(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const
         const int al = o & 15, bl = o >> 4;
         const int mt = bl >> 4, ln = ((al >> 2) << 4) | (bl & 15), i = al & 3;
         float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w)
+        for (int w = 0; w < WAVES; ++w)   // fixed order: deterministic
             v += red[w][mt][i][ln];
         const int n = n0 + al, m = bl;
         if (n < N && m < M) {
@@ -190,36 +195,39 @@ dense_tiled(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const 
 
     constexpr int A_CHUNKS = BA * 8 / 256, B_CHUNKS = BB * 8 / 256;
     const int chunk_col = (tid & 7) * 16;   // byte column of this thread's chunks in a step
-    const uint8_t* ga[A_CHUNKS];
+    const Buf bufW(W, (uint32_t)N * (uint32_t)row_bytes);   // rows past N / M read as zeros
+    const Buf bufX(X, (uint32_t)M * (uint32_t)row_bytes);
+    uint32_t ga[A_CHUNKS];
     int la[A_CHUNKS];
-    bool oka[A_CHUNKS];
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
         int c = tid + j * 256, row = c >> 3, col = c & 7;
-        oka[j] = a0 + row < N;
-        ga[j] = W + (int64_t)(oka[j] ? a0 + row : 0) * row_bytes + col * 16;
+        ga[j] = (uint32_t)(a0 + row) * (uint32_t)row_bytes + col * 16;
         la[j] = row * STRIDE + col * 16;
     }
-    const uint8_t* gb[B_CHUNKS];
+    uint32_t gb[B_CHUNKS];
     int lb[B_CHUNKS];
-    bool okb[B_CHUNKS];
 #pragma unroll
     for (int j = 0; j < B_CHUNKS; ++j) {
         int c = tid + j * 256, row = c >> 3, col = c & 7;
-        okb[j] = b0 + row < M;
-        gb[j] = X + (int64_t)(okb[j] ? b0 + row : 0) * row_bytes + col * 16;
+        gb[j] = (uint32_t)(b0 + row) * (uint32_t)row_bytes + col * 16;
         lb[j] = row * STRIDE + col * 16;
     }
     const uint4 zero = make_uint4(0, 0, 0, 0);
     uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-    auto gload = [&](int s) {
+    // K loop rotated per workgroup (as in the sparse kernel)
+    const int rot = (int)((blockIdx.x * 13u) % (unsigned)steps);
+    auto gload = [&](int sl) {
+        const int s = sl + rot >= steps ? sl + rot - steps : sl + rot;
+        // a 16-byte chunk past K (a partial last step) reads as zeros
         const bool in = (int64_t)s * STEP_BYTES + chunk_col < row_bytes;
+        const uint32_t ks = in ? (uint32_t)s * STEP_BYTES : kOOB;
 #pragma unroll
         for (int j = 0; j < A_CHUNKS; ++j)
-            ra[j] = (in && oka[j]) ? ld16(ga[j] + (int64_t)s * STEP_BYTES) : zero;
+            ra[j] = bufW.ld16(ga[j] + ks);
 #pragma unroll
         for (int j = 0; j < B_CHUNKS; ++j)
-            rb[j] = (in && okb[j]) ? ld16(gb[j] + (int64_t)s * STEP_BYTES) : zero;
+            rb[j] = bufX.ld16(gb[j] + ks);
     };
     auto lstore = [&](int buf) {
 #pragma unroll
@@ -315,23 +323,16 @@ hipError_t dispatch(const DenseArgs& g, hipStream_t s, const char** kname) {
         int waves = 16;
         while (waves > 4 && ((int64_t)tiles16 * waves > 8192 || steps < waves * 2))
             waves >>= 1;
-#define DENSE_SKINNY(MT, W_, U)                                                                      \
+#define DENSE_SKINNY(MT, U)                                                                          \
     do {                                                                                             \
-        hipLaunchKernelGGL((dense_skinny<DT, OUT, MT, W_, U>), dim3(tiles16), dim3(W_ * 64), 0, s, W, \
+        hipLaunchKernelGGL((dense_skinny<DT, OUT, MT, U>), dim3(tiles16), dim3(waves * 64), 0, s, W,   \
                            X, g.scale_x, g.scale_w, g.Y, N, M, g.K);                                 \
-        if (kname) *kname = "dense_skinny_m" #MT "_w" #W_;                                           \
-    } while (0)
-#define DENSE_SKINNY_W(MT, U)                    \
-    do {                                         \
-        if (waves == 16) DENSE_SKINNY(MT, 16, U); \
-        else if (waves == 8) DENSE_SKINNY(MT, 8, U); \
-        else DENSE_SKINNY(MT, 4, U);             \
+        if (kname) *kname = "dense_skinny_m" #MT;                                                    \
     } while (0)
         const int mt = (M + 15) / 16;
-        if (mt <= 1) DENSE_SKINNY_W(1, 4);
-        else if (mt == 2) DENSE_SKINNY_W(2, 2);
-        else DENSE_SKINNY_W(4, 2);
-#undef DENSE_SKINNY_W
+        if (mt <= 1) DENSE_SKINNY(1, 4);
+        else if (mt == 2) DENSE_SKINNY(2, 2);
+        else DENSE_SKINNY(4, 2);
 #undef DENSE_SKINNY
     } else {
         constexpr int FA = 2, FB = 2, BA = 2 * FA * 32, BB = 2 * FB * 32;

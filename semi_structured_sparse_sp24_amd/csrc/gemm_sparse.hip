@@ -24,65 +24,73 @@
 namespace sp24 {
 namespace {
 
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-constexpr uint32_t kLegalIdx = 0x44444444u;  // positions (0,1) in every group: used for zero padding rows
-
 // ------------------------------------------------------------------ skinny
-template <sp24_dtype DT, sp24_dtype OUT, int MT, int WAVES, int U>
-__global__ void __launch_bounds__(WAVES * 64)
+constexpr int kMaxWaves = 16;
+
+template <sp24_dtype DT, sp24_dtype OUT, int MT, int U>
+__global__ void __launch_bounds__(kMaxWaves * 64)
 sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
             const uint8_t* __restrict__ B, const float* __restrict__ sa, const float* __restrict__ sb,
             void* __restrict__ Y, int RA, int RB, int64_t K, int64_t sya, int64_t syb) {
     using L = StepLayout<DT>;
     using Op = SparseOp<DT>;
-    __shared__ float red[WAVES][MT][4][64];
+    __shared__ float red[kMaxWaves][MT][4][64];
 
+    const int WAVES = blockDim.x >> 6;   // 4, 8 or 16: the waves split K
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, kg = lane >> 4;
     const int a0 = blockIdx.x * 16;
     const int steps = (int)(K / L::KSTEP);
-    const int64_t a_row_bytes = K / 2 * L::ELEM, b_row_bytes = K * L::ELEM, mw = K / 32;
+    const uint32_t a_row_bytes = (uint32_t)(K / 2 * L::ELEM), b_row_bytes = (uint32_t)(K * L::ELEM);
+    const uint32_t m_row_bytes = (uint32_t)(K / 8);
 
-    const int arow = a0 + r;
-    const bool a_ok = arow < RA;
-    const uint8_t* ap = av + (int64_t)(a_ok ? arow : 0) * a_row_bytes + L::a_off(kg);
-    const uint32_t* mp = am + (int64_t)(a_ok ? arow : 0) * mw + L::meta_word(kg);
+    // buffers sized to the operands: rows past RA / RB read as zeros
+    const Buf bufA(av, (uint32_t)RA * a_row_bytes);
+    const Buf bufM(am, (uint32_t)RA * m_row_bytes);
+    const Buf bufB(B, (uint32_t)RB * b_row_bytes);
+    const uint32_t a_base = (uint32_t)(a0 + r) * a_row_bytes + L::a_off(kg);
+    const uint32_t m_base = (uint32_t)(a0 + r) * m_row_bytes + 4 * L::meta_word(kg);
     const int msh = L::meta_shift(kg);
-    const uint8_t* bp[MT];
-    bool b_ok[MT];
+    uint32_t b_base[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        int brow = mt * 16 + r;
-        b_ok[mt] = brow < RB;
-        bp[mt] = B + (int64_t)(b_ok[mt] ? brow : 0) * b_row_bytes;
-    }
+    for (int mt = 0; mt < MT; ++mt)
+        b_base[mt] = (uint32_t)(mt * 16 + r) * b_row_bytes;
 
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
         acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int s0 = wave; s0 < steps; s0 += WAVES * U) {
+    // Each wave takes a contiguous chunk of K steps, so each of its rows is
+    // read as one contiguous run; the whole K loop of a workgroup starts at a
+    // rotated step so that concurrent workgroups read different column
+    // offsets (rows are power-of-two strides apart).
+    const int chunk = (steps + WAVES - 1) / WAVES;
+    const int rot = (int)((blockIdx.x * 13u) % (unsigned)max(steps, 1));
+    for (int i0 = 0; i0 < chunk; i0 += U) {
         uint4 a[U], b0[U][MT], b1[U][MT];
         uint32_t idx[U];
+        bool live[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s = s0 + u * WAVES;
-            const bool in = s < steps;
-            a[u] = (in && a_ok) ? ld16(ap + (int64_t)s * L::A_STEP_BYTES) : zero;
-            idx[u] = (in && a_ok) ? (mp[(int64_t)s * L::META_WORDS] >> msh) : kLegalIdx;
+            const int sl = wave * chunk + i0 + u;
+            live[u] = i0 + u < chunk && sl < steps;
+            int s = sl + rot;
+            s = s >= steps ? s - steps : s;
+            const uint32_t sa_off = live[u] ? a_base + (uint32_t)s * L::A_STEP_BYTES : kOOB;
+            const uint32_t sm_off = live[u] ? m_base + (uint32_t)s * (4 * L::META_WORDS) : kOOB;
+            a[u] = bufA.ld16(sa_off);
+            idx[u] = bufM.ld4(sm_off) >> msh;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const uint8_t* p = bp[mt] + (int64_t)s * L::B_STEP_BYTES;
-                b0[u][mt] = (in && b_ok[mt]) ? ld16(p + L::b_off0(kg)) : zero;
-                b1[u][mt] = (in && b_ok[mt]) ? ld16(p + L::b_off1(kg)) : zero;
+                const uint32_t o = live[u] ? b_base[mt] + (uint32_t)s * L::B_STEP_BYTES : kOOB;
+                b0[u][mt] = bufB.ld16(o + L::b_off0(kg));
+                b1[u][mt] = bufB.ld16(o + L::b_off1(kg));
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (s0 + u * WAVES < steps) {
+            if (live[u]) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     acc[mt] = Op::mma(a[u], b0[u][mt], b1[u][mt], idx[u], acc[mt]);
@@ -102,8 +110,7 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
         const int al = o & 15, bl = o >> 4;
         const int mt = bl >> 4, ln = ((al >> 2) << 4) | (bl & 15), i = al & 3;
         float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w)
+        for (int w = 0; w < WAVES; ++w)   // fixed order: deterministic
             v += red[w][mt][i][ln];
         const int ar = a0 + al, br = bl;
         if (ar < RA && br < RB) {
@@ -144,53 +151,57 @@ sp24_tiled(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
     const int ta = blockIdx.x % tiles_a, tb = blockIdx.x / tiles_a;
     const int a0 = ta * BA, b0 = tb * BB;
     const int steps = (int)(K / L::KSTEP);
-    const int64_t a_row_bytes = K / 2 * L::ELEM, b_row_bytes = K * L::ELEM, mw = K / 32;
 
-    // global -> LDS assignment: A chunks of 16 B (4 per row), B chunks (8 per row), meta words
+    // global -> LDS assignment: A chunks of 16 B (4 per row), B chunks (8 per
+    // row), metadata words.  Buffers are sized to the operands, so rows past
+    // RA / RB read as zeros.
+    const uint32_t a_row_bytes = (uint32_t)(K / 2 * L::ELEM), b_row_bytes = (uint32_t)(K * L::ELEM);
+    const uint32_t m_row_bytes = (uint32_t)(K / 8);
+    const Buf bufA(av, (uint32_t)RA * a_row_bytes);
+    const Buf bufM(am, (uint32_t)RA * m_row_bytes);
+    const Buf bufB(B, (uint32_t)RB * b_row_bytes);
     constexpr int A_CHUNKS = BA * 4 / 256, B_CHUNKS = BB * 8 / 256, M_WORDS = (BA * MWS + 255) / 256;
-    const uint8_t* ga[A_CHUNKS];
+    uint32_t ga[A_CHUNKS];
     int la[A_CHUNKS];
-    bool oka[A_CHUNKS];
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
         int c = tid + j * 256, row = c >> 2, col = c & 3;
-        oka[j] = a0 + row < RA;
-        ga[j] = av + (int64_t)(oka[j] ? a0 + row : 0) * a_row_bytes + col * 16;
+        ga[j] = (uint32_t)(a0 + row) * a_row_bytes + col * 16;
         la[j] = row * S::A_STRIDE + col * 16;
     }
-    const uint8_t* gb[B_CHUNKS];
+    uint32_t gb[B_CHUNKS];
     int lb[B_CHUNKS];
-    bool okb[B_CHUNKS];
 #pragma unroll
     for (int j = 0; j < B_CHUNKS; ++j) {
         int c = tid + j * 256, row = c >> 3, col = c & 7;
-        okb[j] = b0 + row < RB;
-        gb[j] = B + (int64_t)(okb[j] ? b0 + row : 0) * b_row_bytes + col * 16;
+        gb[j] = (uint32_t)(b0 + row) * b_row_bytes + col * 16;
         lb[j] = row * S::B_STRIDE + col * 16;
     }
-    const uint32_t* gm[M_WORDS];
-    bool okm[M_WORDS], usem[M_WORDS];
+    uint32_t gm[M_WORDS];
+    bool usem[M_WORDS];
 #pragma unroll
     for (int j = 0; j < M_WORDS; ++j) {
         int c = tid + j * 256, row = c / MWS, w = c % MWS;
         usem[j] = c < BA * MWS;
-        okm[j] = usem[j] && a0 + row < RA;
-        gm[j] = am + (int64_t)(okm[j] ? a0 + row : 0) * mw + w;
+        gm[j] = (uint32_t)(a0 + row) * m_row_bytes + 4 * w;
     }
 
-    const uint4 zero = make_uint4(0, 0, 0, 0);
     uint4 ra[A_CHUNKS], rb[B_CHUNKS];
     uint32_t rm[M_WORDS];
-    auto gload = [&](int s) {
+    // K loop starts at a per-workgroup rotated step (spreads concurrent
+    // workgroups over memory channels; the sum order is fixed per shape)
+    const int rot = (int)((blockIdx.x * 13u) % (unsigned)steps);
+    auto gload = [&](int sl) {
+        const uint32_t s = (uint32_t)(sl + rot >= steps ? sl + rot - steps : sl + rot);
 #pragma unroll
         for (int j = 0; j < A_CHUNKS; ++j)
-            ra[j] = oka[j] ? ld16(ga[j] + (int64_t)s * L::A_STEP_BYTES) : zero;
+            ra[j] = bufA.ld16(ga[j] + s * L::A_STEP_BYTES);
 #pragma unroll
         for (int j = 0; j < B_CHUNKS; ++j)
-            rb[j] = okb[j] ? ld16(gb[j] + (int64_t)s * L::B_STEP_BYTES) : zero;
+            rb[j] = bufB.ld16(gb[j] + s * L::B_STEP_BYTES);
 #pragma unroll
         for (int j = 0; j < M_WORDS; ++j)
-            rm[j] = okm[j] ? gm[j][(int64_t)s * MWS] : kLegalIdx;
+            rm[j] = bufM.ld4(usem[j] ? gm[j] + s * (4 * MWS) : kOOB);
     };
     auto lstore = [&](int buf) {
 #pragma unroll
@@ -284,24 +295,19 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
         int waves = 16;
         while (waves > 4 && ((int64_t)tiles16 * waves > 8192 || steps < waves * 2))
             waves >>= 1;
-#define SP24_SKINNY(MT, W, U)                                                                         \
+#define SP24_SKINNY(MT, U)                                                                            \
     do {                                                                                              \
-        hipLaunchKernelGGL((sp24_skinny<DT, OUT, MT, W, U>), dim3(tiles16), dim3(W * 64), 0, s, av,     \
+        hipLaunchKernelGGL((sp24_skinny<DT, OUT, MT, U>), dim3(tiles16), dim3(waves * 64), 0, s, av,    \
                            g.a_meta, b, g.scale_a, g.scale_b, g.Y, RA, RB, g.K, sya, syb);            \
-        if (kname) *kname = "sp24_skinny_m" #MT "_w" #W;                                              \
-    } while (0)
-#define SP24_SKINNY_W(MT, U)                   \
-    do {                                       \
-        if (waves == 16) SP24_SKINNY(MT, 16, U); \
-        else if (waves == 8) SP24_SKINNY(MT, 8, U); \
-        else SP24_SKINNY(MT, 4, U);            \
+        if (kname) *kname = "sp24_skinny_m" #MT;                                                      \
     } while (0)
         const int mt = (RB + 15) / 16;
-        if (mt <= 1) SP24_SKINNY_W(1, 4);
-        else if (mt == 2) SP24_SKINNY_W(2, 2);
-        else SP24_SKINNY_W(4, 2);
-#undef SP24_SKINNY_W
+        if (mt <= 1) SP24_SKINNY(1, 4);
+        else if (mt == 2) SP24_SKINNY(2, 2);
+        else SP24_SKINNY(4, 2);
 #undef SP24_SKINNY
+    } else if ((int64_t)((RA + 255) / 256) * ((RB + 255) / 256) >= 192) {
+        return launch_sp24_gemm_big(g, s, kname);
     } else {
         constexpr int FA = 4, FB = 4;
         using S = TiledShape<FA, FB>;

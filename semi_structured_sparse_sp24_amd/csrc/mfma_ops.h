@@ -36,6 +36,26 @@
 
 namespace sp24 {
 
+// Raw buffer access over one operand.  The descriptor's size is the operand's
+// byte size, and the hardware returns zeros for any offset at or past it, so
+// rows past the end of a matrix and chunks masked with kOOB read as zeros
+// without branches.  Operands are limited to 2 GiB each (checked on the host).
+constexpr uint32_t kOOB = 0x80000000u;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ Buf(const void* p, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000)) {}
+    __device__ __forceinline__ uint4 ld16(uint32_t off) const {
+        u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    __device__ __forceinline__ uint32_t ld4(uint32_t off) const {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    }
+};
+
 template <sp24_dtype DT>
 struct SparseOp;
 

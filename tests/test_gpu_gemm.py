@@ -135,6 +135,18 @@ def test_exact_integer_bitwise(dt, M, N, K):
         assert np.array_equal(to_host(Yd, oracle.F16), oracle.encode(oracle.F16, R))
 
 
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.E4M3])
+@pytest.mark.parametrize("M,N,K", [(3, 40, 96), (16, 17, 200), (100, 70, 112), (130, 129, 1040)])
+def test_dense_accepts_k_the_sparse_path_rejects(dt, M, N, K):
+    """The dense fallback takes any K filling whole 16-byte row chunks, so a
+    partial last K step is read as zeros."""
+    if dt == oracle.E4M3:
+        K = (K + 15) // 16 * 16
+    say("dense K tail", dt, M, N, K)
+    Y, R, _ = _dense(dt, oracle.F32, M, N, K, seed=K + M, integer=True, prune_w=False)
+    assert np.array_equal(Y, R)
+
+
 def test_one_hot_rows_read_back_weights():
     """X = identity rows: Y[m, :] is column m of the decompressed W, which
     checks every metadata position and word through the sparse MMA."""
