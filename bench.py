@@ -61,6 +61,29 @@ def compress_bytes(R, K, eb):
     return R * K * eb + R * K * eb // 2 + R * K // 8
 
 
+def traffic_per_launch(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload`, from the FETCH_SIZE and WRITE_SIZE counter runs
+    recorded in profiles/traffic.md (scaled by the same counters' reading for a copy of known size).
+    None when no record exists or when the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        # | kernel | workload | source sha256 (12) | bytes per launch | ...
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) < 4 or cells[0] != kernel or cells[1] != workload:
+            continue
+        src = os.path.join(ROOT, "semi_structured_sparse_sp24_amd", "csrc", cells[2].split(":")[0])
+        if not os.path.exists(src):
+            return None
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:12]
+        if cells[2].split(":")[1] != digest:
+            return None
+        return float(cells[3])
+    return None
+
+
 class Timer:
     """HIP events on torch's current stream (the one the library launches on)."""
 
@@ -282,21 +305,42 @@ def main():
     speedup = tot["dense_t"] / tot["sparse_t"]
     compress_gbps = tot["compress_bytes"] / tot["compress_t"] / 1e3
 
-    # roofline of the dominant kernel: the sparse GEMM (every launch in the step is the same kernel
-    # family; achieved = algorithmic bytes or flops per launch / mean launch duration)
-    avg_us = tot["sparse_t"] / tot["sparse_launches"]
-    if workload in ("decode", "fp8", "tiny") and max(it["M"] for c in cases for it in c["ms"]) <= 64:
-        achieved = tot["sparse_bytes"] / tot["sparse_t"] / 1e3
+    # roofline of the dominant kernel: the sparse GEMM kernel (by name, as the dispatch picks it per
+    # shape) with the largest share of the step's sparse GEMM time; achieved = its algorithmic bytes
+    # (HBM-bound decode) or flops (MFMA-bound prefill) per launch / its mean launch duration
+    per_kernel = {}
+    for c in cases:
+        for it in c["ms"]:
+            M, N, K = it["M"], c["N"], c["K"]
+            which = sp.SPARSE_X if workload == "online" else sp.SPARSE_W
+            name = sp.gemm_kernel(True, which, TORCH[dt], it["Y"].dtype, M, N, K)
+            ts = times[("sparse", c["s"], it["j"])]
+            sparse_rows = M if workload == "online" else N
+            k = per_kernel.setdefault(name, {"t": 0.0, "n": 0, "bytes": 0.0, "flops": 0.0})
+            k["t"] += sum(ts)
+            k["n"] += len(ts)
+            k["bytes"] += sparse_gemm_bytes(M, N, K, eb, out_eb, sparse_rows, scales) * len(ts)
+            k["flops"] += 2.0 * M * N * K * len(ts)
+    kname = max(per_kernel, key=lambda n: per_kernel[n]["t"])
+    k = per_kernel[kname]
+    avg_us = k["t"] / k["n"]
+    hbm_bound = max(it["M"] for c in cases for it in c["ms"]) <= 64
+    if hbm_bound:
+        achieved = k["bytes"] / k["t"] / 1e3
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": "sp24_skinny", "bytes_per_launch": round(tot["sparse_bytes"] / tot["sparse_launches"]),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_per_launch(kname, workload),
+                "kernel": kname, "launches": k["n"], "bytes_per_launch": round(k["bytes"] / k["n"]),
                 "avg_launch_us": round(avg_us, 3)}
     else:
         peak = SPARSE_PEAK_TFLOPS[dt]
-        roof = {"bound": "mfma", "achieved": round(value, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(value / peak, 4), "traffic": None, "kernel": "sp24_tiled",
-                "flops_per_launch": round(tot["flops"] / tot["sparse_launches"]),
+        achieved = k["flops"] / k["t"] / 1e6
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic_per_launch(kname, workload),
+                "kernel": kname, "launches": k["n"], "flops_per_launch": round(k["flops"] / k["n"]),
                 "avg_launch_us": round(avg_us, 3)}
+    roof["kernels"] = {n: {"launches": v["n"], "avg_launch_us": round(v["t"] / v["n"], 3),
+                           "share": round(v["t"] / tot["sparse_t"], 3)} for n, v in per_kernel.items()}
 
     tactics = []
     if not args.no_tactic:

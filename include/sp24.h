@@ -159,6 +159,18 @@ sp24_status dense_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N
                        const float *scale_x, const float *scale_w,
                        void *Y, hipStream_t stream);
 
+/*
+ * The name of the kernel that sp24_gemm (sparse != 0) or dense_gemm
+ * (sparse == 0) launches for this shape and dtype, without launching
+ * anything: a pure host function, no HIP call.  The same names appear in
+ * sp24_tactic.kernel and, as template instantiations, in profiler traces.
+ * Returns NULL when the call would be rejected on its dtypes or shape
+ * (including SP24_E_ALIGN on K), "none" when M or N is 0 and "fill_zero"
+ * when K is 0.  The returned string is static; do not free it.
+ */
+const char *sp24_gemm_kernel(int sparse, sp24_operand which, sp24_dtype in_dt,
+                             sp24_dtype out_dt, int64_t M, int64_t N, int64_t K);
+
 /* Per-shape tactic record ("Production 2:4 Structured Sparsity for LLMs",
  * section "Sparse Tactic Audit": eligible / selected / reason per layer). */
 typedef struct {

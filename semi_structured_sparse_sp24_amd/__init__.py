@@ -12,6 +12,7 @@ PyTorch fallback: if the library is missing, every call raises.
   dense_gemm(x, w, ...)        -> Y = X W^T, the dense baseline
   select_tactic(...)           -> per-shape sparse-or-dense record
   tactic_decide(...)           -> the decision rule on given timings (host only)
+  gemm_kernel(...)             -> name of the kernel a GEMM call would launch (host only)
 """
 from __future__ import annotations
 
@@ -57,6 +58,7 @@ SIGNATURES = {
                                   _vp, _i32, _i32, _vp, ctypes.POINTER(Tactic)]),
     "sp24_tactic_decide": (_i32, [_i32, ctypes.POINTER(_dbl), _i32, ctypes.POINTER(_dbl), _i32,
                                   ctypes.POINTER(Tactic)]),
+    "sp24_gemm_kernel": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i64, _i64, _i64]),
 }
 
 _lib = None
@@ -180,6 +182,12 @@ def tactic_decide(eligible: bool, t_sparse, t_dense) -> dict:
     st = lib().sp24_tactic_decide(int(eligible), ts, len(t_sparse), td, len(t_dense), ctypes.byref(rec))
     _check("sp24_tactic_decide", st)
     return rec.as_dict()
+
+
+def gemm_kernel(sparse: bool, which: int, in_dtype, out_dtype, M: int, N: int, K: int):
+    """Name of the kernel sp24_gemm (sparse) or dense_gemm launches for this shape; None if rejected."""
+    name = lib().sp24_gemm_kernel(int(sparse), which, DTYPE_CODE[in_dtype], DTYPE_CODE[out_dtype], M, N, K)
+    return None if name is None else name.decode()
 
 
 def version() -> str:

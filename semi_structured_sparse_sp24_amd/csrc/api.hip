@@ -40,9 +40,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Shared checks of the two GEMM entry points.  Returns SP24_OK when the
 // shape is eligible for the MFMA kernels.
-sp24_status check_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K,
-                       std::initializer_list<const void*> required, const void* Y,
-                       const float* sx, const float* sw, bool sparse) {
+// Checks on dtypes and sizes alone (no pointer is looked at).
+sp24_status check_shape(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K, bool sparse) {
     if (!is_input_dtype(in_dt) || !out_ok(in_dt, out_dt))
         return SP24_E_DTYPE;
     if (M < 0 || N < 0 || K < 0 || K % 4 != 0)
@@ -57,15 +56,30 @@ sp24_status check_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N
         return SP24_E_SHAPE;
     if (M == 0 || N == 0)
         return SP24_OK;
-    if (!Y)
-        return SP24_E_NULL;
-    if (K > 0)
-        for (const void* p : required)
-            if (!p)
-                return SP24_E_NULL;
     // sparse: whole MFMA steps; dense: whole 16-byte chunks of every row
     if (K % (sparse ? gemm_k_tile(in_dt) : 16 / elem_bytes(in_dt)) != 0)
         return SP24_E_ALIGN;
+    return SP24_OK;
+}
+
+sp24_status check_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K,
+                       std::initializer_list<const void*> required, const void* Y,
+                       const float* sx, const float* sw, bool sparse) {
+    if (!is_input_dtype(in_dt) || !out_ok(in_dt, out_dt))
+        return SP24_E_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0)
+        return SP24_E_SHAPE;
+    if (M > 0 && N > 0) {
+        if (!Y)
+            return SP24_E_NULL;
+        if (K > 0)
+            for (const void* p : required)
+                if (!p)
+                    return SP24_E_NULL;
+    }
+    sp24_status st = check_shape(in_dt, out_dt, M, N, K, sparse);
+    if (st != SP24_OK || M == 0 || N == 0)
+        return st;
     if (!aligned16(Y) || ((uintptr_t)sx & 3u) || ((uintptr_t)sw & 3u))
         return SP24_E_ALIGN;
     for (const void* p : required)
@@ -188,6 +202,40 @@ static sp24_status dense_impl(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, in
     g.scale_w = scale_w;
     g.Y = Y;
     return launch_dense_gemm(g, stream, kname) == hipSuccess ? SP24_OK : SP24_E_HIP;
+}
+
+SP24_API const char* sp24_gemm_kernel(int sparse, sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt,
+                                     int64_t M, int64_t N, int64_t K) {
+    if (sparse && which != SP24_SPARSE_W && which != SP24_SPARSE_X)
+        return nullptr;
+    if (check_shape(in_dt, out_dt, M, N, K, sparse != 0) != SP24_OK)
+        return nullptr;
+    if (M == 0 || N == 0)
+        return "none";
+    if (K == 0)
+        return "fill_zero";
+    const char* name = nullptr;
+    if (sparse) {
+        GemmArgs g{};
+        g.in_dt = in_dt;
+        g.out_dt = out_dt;
+        g.M = M;
+        g.N = N;
+        g.K = K;
+        g.a_is_w = which == SP24_SPARSE_W;
+        g.dry = true;
+        launch_sp24_gemm(g, nullptr, &name);
+    } else {
+        DenseArgs g{};
+        g.in_dt = in_dt;
+        g.out_dt = out_dt;
+        g.M = M;
+        g.N = N;
+        g.K = K;
+        g.dry = true;
+        launch_dense_gemm(g, nullptr, &name);
+    }
+    return name;
 }
 
 SP24_API sp24_status sp24_gemm(sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt, int64_t M,

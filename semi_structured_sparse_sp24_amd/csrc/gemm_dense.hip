@@ -325,8 +325,9 @@ hipError_t dispatch(const DenseArgs& g, hipStream_t s, const char** kname) {
             waves >>= 1;
 #define DENSE_SKINNY(MT, U)                                                                          \
     do {                                                                                             \
-        hipLaunchKernelGGL((dense_skinny<DT, OUT, MT, U>), dim3(tiles16), dim3(waves * 64), 0, s, W,   \
-                           X, g.scale_x, g.scale_w, g.Y, N, M, g.K);                                 \
+        if (!g.dry)                                                                                  \
+            hipLaunchKernelGGL((dense_skinny<DT, OUT, MT, U>), dim3(tiles16), dim3(waves * 64), 0, s,  \
+                               W, X, g.scale_x, g.scale_w, g.Y, N, M, g.K);                          \
         if (kname) *kname = "dense_skinny_m" #MT;                                                    \
     } while (0)
         const int mt = (M + 15) / 16;
@@ -334,14 +335,17 @@ hipError_t dispatch(const DenseArgs& g, hipStream_t s, const char** kname) {
         else if (mt == 2) DENSE_SKINNY(2, 2);
         else DENSE_SKINNY(4, 2);
 #undef DENSE_SKINNY
+    } else if ((int64_t)((N + 255) / 256) * ((M + 255) / 256) >= 192) {
+        return launch_dense_gemm_big(g, s, kname);
     } else {
         constexpr int FA = 2, FB = 2, BA = 2 * FA * 32, BB = 2 * FB * 32;
         const int tiles_n = (N + BA - 1) / BA, tiles_m = (M + BB - 1) / BB;
-        hipLaunchKernelGGL((dense_tiled<DT, OUT, FA, FB>), dim3(tiles_n * tiles_m), dim3(256), 0, s, W, X,
-                           g.scale_x, g.scale_w, g.Y, N, M, g.K, tiles_n);
+        if (!g.dry)
+            hipLaunchKernelGGL((dense_tiled<DT, OUT, FA, FB>), dim3(tiles_n * tiles_m), dim3(256), 0, s, W,
+                               X, g.scale_x, g.scale_w, g.Y, N, M, g.K, tiles_n);
         if (kname) *kname = "dense_tiled_128x128";
     }
-    return hipGetLastError();
+    return g.dry ? hipSuccess : hipGetLastError();
 }
 
 }  // namespace

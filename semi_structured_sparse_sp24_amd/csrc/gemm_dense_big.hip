@@ -1,0 +1,235 @@
+// gemm_dense_big.hip -- dense GEMM baseline Y = X * W^T for large M, built
+// the same way as the large sparse kernel so that the tactic comparison is
+// between kernels of the same construction ("Production 2:4 Structured
+// Sparsity for LLMs", section "Sparse Tactic Audit").
+//
+//   - tile 256 (W rows) x 256 (X rows); 4 waves in a 2 x 2 grid, each owning
+//     128 x 128 = 4 x 4 fragments of v_mfma_f32_32x32x16 (16-bit) or
+//     v_mfma_scale_f32_32x32x64_f8f6f4 (fp8, unit scales);
+//   - one stage = one 128-byte slice of every row of both operands (64 K for
+//     16-bit, 128 K for fp8): 64 KB; two stages in LDS, filled by direct
+//     global->LDS loads while the other is consumed;
+//   - 16-byte chunks XOR-swizzled by row for conflict-free fragment reads;
+//   - XCD-aware grouped tile order, K start rotated per group.
+// Any K with whole 16-byte row chunks is accepted: chunks past the end of a
+// row read as zeros.
+#include "mfma_ops.h"
+
+namespace sp24 {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kBA = 256, kBB = 256, kThreads = 256;
+constexpr int kStage = 256 * 128;   // bytes per operand per stage
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+template <sp24_dtype DT>
+struct Dense32;
+template <>
+struct Dense32<SP24_BF16> {
+    static constexpr int KSTEP = 64, SUB = 4, CHUNKS = 1;   // per instruction: 1 chunk of 16 B per lane
+    __device__ static __forceinline__ f32x16 mma(const uint4* a, const uint4* b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
+                                                       __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+    }
+};
+template <>
+struct Dense32<SP24_F16> {
+    static constexpr int KSTEP = 64, SUB = 4, CHUNKS = 1;
+    __device__ static __forceinline__ f32x16 mma(const uint4* a, const uint4* b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[0]),
+                                                      __builtin_bit_cast(f16x8, b[0]), c, 0, 0, 0);
+    }
+};
+template <>
+struct Dense32<SP24_E4M3> {
+    static constexpr int KSTEP = 128, SUB = 2, CHUNKS = 2;  // 32 B per lane per instruction
+    __device__ static __forceinline__ f32x16 mma(const uint4* a, const uint4* b, f32x16 c) {
+        struct { uint4 x, y; } aa = {a[0], a[1]}, bb = {b[0], b[1]};
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            __builtin_bit_cast(i32x8, aa), __builtin_bit_cast(i32x8, bb), c, 0, 0, 0, 0x7f, 0, 0x7f);
+    }
+};
+
+template <sp24_dtype DT, sp24_dtype OUT>
+__global__ void __launch_bounds__(kThreads, 1)
+dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
+          const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K, int tiles_a,
+          int tiles_b) {
+    using Op = Dense32<DT>;
+    constexpr int LOADS = 2 * kStage / 1024 / 4;   // per wave per stage: 8 (W) + 8 (X)
+    __shared__ __attribute__((aligned(1024))) uint8_t a0s[kStage], a1s[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t b0s[kStage], b1s[kStage];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, kg = lane >> 5;
+    const int wa = wave >> 1, wb = wave & 1;
+
+    // ---- tile order: XCD-aware, grouped 4 W tiles x all X tiles
+    const int nwg = gridDim.x;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int per_xcd = (nwg + 7) >> 3, full = nwg & 7 ? (nwg & 7) : 8;
+    const int t = xcd < full ? xcd * per_xcd + local : full * per_xcd + (xcd - full) * (per_xcd - 1) + local;
+    constexpr int G = 4;
+    const int group = t / (G * tiles_b), within = t - group * G * tiles_b;
+    const int g_rows = min(G, tiles_a - group * G);
+    const int ta = group * G + within % g_rows, tb = within / g_rows;
+    const int a0 = ta * kBA, b0 = tb * kBB;
+
+    const uint32_t row_bytes = (uint32_t)K * (DT == SP24_E4M3 ? 1 : 2);
+    const int steps = (int)((row_bytes + 127) / 128);   // the last may be partial
+    const Buf bufW(W, (uint32_t)N * row_bytes);           // rows past N / M read as zeros
+    const Buf bufX(X, (uint32_t)M * row_bytes);
+
+    // ---- this wave's loads: 8 x 1 KiB of W rows and 8 of X rows per stage
+    uint32_t ga[8], gb[8];
+    int gc[8];   // byte column of the chunk each lane fetches (for the partial last step)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int row = 8 * (8 * wave + j) + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        gc[j] = 16 * c;
+        ga[j] = (uint32_t)(a0 + row) * row_bytes + 16 * c;
+        gb[j] = (uint32_t)(b0 + row) * row_bytes + 16 * c;
+    }
+    const int rot = (int)(((unsigned)group * 13u) % (unsigned)steps);
+    auto issue = [&](uint8_t* as, uint8_t* bs, int sl) {
+        int s = sl + rot;
+        s = s >= steps ? s - steps : s;
+        const bool live = sl < steps;
+        const uint32_t so = (uint32_t)s * 128;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool in = live && so + gc[j] < row_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufW.r, (lds_void*)(as + 1024 * (8 * wave + j)), 16,
+                                                     (int)(in ? ga[j] : kOOB), (int)(in ? so : 0u), 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool in = live && so + gc[j] < row_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufX.r, (lds_void*)(bs + 1024 * (8 * wave + j)), 16,
+                                                     (int)(in ? gb[j] : kOOB), (int)(in ? so : 0u), 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = (f32x16){};
+
+    const int swz = (r >> 1) & 7;
+    auto compute = [&](const uint8_t* as, const uint8_t* bs) {
+#pragma unroll
+        for (int q = 0; q < Op::SUB; ++q) {
+            uint4 fa[4][Op::CHUNKS], fb[4][Op::CHUNKS];
+#pragma unroll
+            for (int h = 0; h < Op::CHUNKS; ++h) {
+                // chunk of K this lane supplies: 16-bit 2q + kg; fp8 4q + 2kg + h
+                const int c = Op::CHUNKS == 1 ? 2 * q + kg : 4 * q + 2 * kg + h;
+                const int off = 16 * (c ^ swz);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    fa[i][h] = *reinterpret_cast<const uint4*>(as + (wa * 128 + i * 32 + r) * 128 + off);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    fb[j][h] = *reinterpret_cast<const uint4*>(bs + (wb * 128 + j * 32 + r) * 128 + off);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = Op::mma(fa[i], fb[j], acc[i][j]);
+        }
+    };
+
+    // ---- two stages: the loads of step s+1 land while step s is consumed;
+    // the step count is padded to even (padded steps read zeros)
+    issue(a0s, b0s, 0);
+    const int steps2 = (steps + 1) / 2 * 2;
+    for (int s = 0; s < steps2; s += 2) {
+        wait_vmcnt_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        issue(a1s, b1s, s + 1);
+        compute(a0s, b0s);
+        wait_vmcnt_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        issue(a0s, b0s, s + 2);
+        compute(a1s, b1s);
+    }
+    wait_vmcnt_lgkm0<0>();
+
+    // ---- epilogue: D[8*(v/4) + 4*kg + v%4][r] of fragment (i, j); a = W row (n), b = X row (m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = b0 + wb * 128 + j * 32 + r;
+            if (m >= M)
+                continue;
+            const float fsx = sx ? sx[m] : 1.f;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int n = a0 + wa * 128 + i * 32 + 8 * h + 4 * kg;
+                if (n >= N)
+                    continue;
+                f32x4 v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    v[q] = acc[i][j][4 * h + q] * fsx * (sw && n + q < N ? sw[n + q] : 1.f);
+                const int64_t off = (int64_t)m * N + n;
+                if (n + 3 < N && (off & 3) == 0) {
+                    store_out4<OUT>(Y, off, v);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (n + q < N)
+                            store_out<OUT>(Y, off + q, v[q]);
+                }
+            }
+        }
+    }
+}
+
+template <sp24_dtype DT, sp24_dtype OUT>
+hipError_t launch(const DenseArgs& g, hipStream_t s, const char** kname) {
+    const int N = (int)g.N, M = (int)g.M;
+    const int tiles_a = (N + kBA - 1) / kBA, tiles_b = (M + kBB - 1) / kBB;
+    if (kname)
+        *kname = "dense_big_256x256";
+    if (g.dry)
+        return hipSuccess;
+    hipLaunchKernelGGL((dense_big<DT, OUT>), dim3(tiles_a * tiles_b), dim3(kThreads), 0, s,
+                       (const uint8_t*)g.W, (const uint8_t*)g.X, g.scale_x, g.scale_w, g.Y, N, M, g.K, tiles_a,
+                       tiles_b);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dense_gemm_big(const DenseArgs& g, hipStream_t s, const char** kname) {
+    switch (g.in_dt) {
+    case SP24_BF16:
+        if (g.out_dt == SP24_BF16) return launch<SP24_BF16, SP24_BF16>(g, s, kname);
+        if (g.out_dt == SP24_F16) return launch<SP24_BF16, SP24_F16>(g, s, kname);
+        return launch<SP24_BF16, SP24_F32>(g, s, kname);
+    case SP24_F16:
+        if (g.out_dt == SP24_F16) return launch<SP24_F16, SP24_F16>(g, s, kname);
+        if (g.out_dt == SP24_BF16) return launch<SP24_F16, SP24_BF16>(g, s, kname);
+        return launch<SP24_F16, SP24_F32>(g, s, kname);
+    case SP24_E4M3:
+        if (g.out_dt == SP24_BF16) return launch<SP24_E4M3, SP24_BF16>(g, s, kname);
+        return launch<SP24_E4M3, SP24_F32>(g, s, kname);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sp24

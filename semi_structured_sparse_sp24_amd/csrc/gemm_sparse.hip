@@ -25,32 +25,62 @@ namespace sp24 {
 namespace {
 
 // ------------------------------------------------------------------ skinny
-constexpr int kMaxWaves = 16;
+constexpr int kMaxWaves = 8;
+constexpr int kGroup = 8;   // K-steps per load group
 
-template <sp24_dtype DT, sp24_dtype OUT, int MT, int U>
-__global__ void __launch_bounds__(kMaxWaves * 64)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Per wave and load group: the group's metadata of the 16 rows (1 KiB for
+// 16-bit steps, 2 KiB for fp8) and, for at most 4 dense rows, the group's
+// slice of those rows (4 x 1 KiB) plus a zero pad read by the empty lanes.
+template <int MWS>
+struct SkinnyLds {
+    static constexpr int META = 16 * kGroup * MWS * 4;
+    static constexpr int XROWS = 4;
+    static constexpr int X = XROWS * kGroup * 128;
+    static constexpr int PER_WAVE = META + X + 32;
+};
+
+template <sp24_dtype DT, sp24_dtype OUT, int MT, bool XLDS>
+__global__ void __launch_bounds__(kMaxWaves * 64, 2)
 sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
             const uint8_t* __restrict__ B, const float* __restrict__ sa, const float* __restrict__ sb,
             void* __restrict__ Y, int RA, int RB, int64_t K, int64_t sya, int64_t syb) {
     using L = StepLayout<DT>;
     using Op = SparseOp<DT>;
+    constexpr int MWS = L::META_WORDS;
+    using SL = SkinnyLds<MWS>;
+    constexpr int M_ROW = kGroup * MWS * 4;         // metadata bytes of one row per group: 64 or 128
+    constexpr int M_CPR = M_ROW / 16;               // 16-byte chunks per row: 4 or 8
+    constexpr int M_LOADS = SL::META / 1024;        // 1 or 2
+    constexpr int M_RPL = 1024 / M_ROW;             // rows per load: 16 or 8
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kMaxWaves][SL::PER_WAVE];
     __shared__ float red[kMaxWaves][MT][4][64];
 
-    const int WAVES = blockDim.x >> 6;   // 4, 8 or 16: the waves split K
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int WAVES = blockDim.x >> 6;   // the waves split K
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, kg = lane >> 4;
     const int a0 = blockIdx.x * 16;
     const int steps = (int)(K / L::KSTEP);
+    const int groups = (steps + kGroup - 1) / kGroup;
     const uint32_t a_row_bytes = (uint32_t)(K / 2 * L::ELEM), b_row_bytes = (uint32_t)(K * L::ELEM);
     const uint32_t m_row_bytes = (uint32_t)(K / 8);
-
-    // buffers sized to the operands: rows past RA / RB read as zeros
-    const Buf bufA(av, (uint32_t)RA * a_row_bytes);
+    const Buf bufA(av, (uint32_t)RA * a_row_bytes);   // rows past RA / RB read as zeros
     const Buf bufM(am, (uint32_t)RA * m_row_bytes);
     const Buf bufB(B, (uint32_t)RB * b_row_bytes);
+    uint8_t* my_m = &lds[wave][0];
+    uint8_t* my_x = &lds[wave][SL::META];
+    uint8_t* zero_pad = &lds[wave][SL::META + SL::X];
+    if (XLDS && lane < 8)
+        reinterpret_cast<uint32_t*>(zero_pad)[lane] = 0u;
+
+    // A: straight from HBM into the operand registers, one 1 KiB load per step
     const uint32_t a_base = (uint32_t)(a0 + r) * a_row_bytes + L::a_off(kg);
-    const uint32_t m_base = (uint32_t)(a0 + r) * m_row_bytes + 4 * L::meta_word(kg);
-    const int msh = L::meta_shift(kg);
+    // metadata: DMA lane roles (row, chunk slot), chunks XOR-swizzled by row
+    const int m_swz_r = M_CPR == 4 ? (r >> 2) & 3 : (r >> 1) & 7;
+    const int msh = L::meta_shift(kg), mwd = L::meta_word(kg);
+    // X through registers (more than 4 dense rows) or through LDS (at most 4)
     uint32_t b_base[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -61,41 +91,77 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
     for (int mt = 0; mt < MT; ++mt)
         acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // Each wave takes a contiguous chunk of K steps, so each of its rows is
-    // read as one contiguous run; the whole K loop of a workgroup starts at a
-    // rotated step so that concurrent workgroups read different column
-    // offsets (rows are power-of-two strides apart).
-    const int chunk = (steps + WAVES - 1) / WAVES;
-    const int rot = (int)((blockIdx.x * 13u) % (unsigned)max(steps, 1));
-    for (int i0 = 0; i0 < chunk; i0 += U) {
-        uint4 a[U], b0[U][MT], b1[U][MT];
-        uint32_t idx[U];
-        bool live[U];
+    // each wave streams a contiguous run of groups; the run of the whole
+    // workgroup starts at a rotated group so that concurrent workgroups read
+    // different column offsets of their (power-of-two strided) rows
+    const int per_wave = (groups + WAVES - 1) / WAVES;
+    const int rot = (int)((blockIdx.x * 5u) % (unsigned)max(groups, 1));
+    for (int gi = 0; gi < per_wave; ++gi) {
+        const int gl = wave * per_wave + gi;
+        if (gl >= groups)
+            break;
+        const int g = gl + rot >= groups ? gl + rot - groups : gl + rot;
+        const int s_first = g * kGroup;
+        const int n_in = min(kGroup, steps - s_first);
+        // ---- issue: A for the group's steps, metadata and X by DMA
+        uint4 fa[kGroup];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int sl = wave * chunk + i0 + u;
-            live[u] = i0 + u < chunk && sl < steps;
-            int s = sl + rot;
-            s = s >= steps ? s - steps : s;
-            const uint32_t sa_off = live[u] ? a_base + (uint32_t)s * L::A_STEP_BYTES : kOOB;
-            const uint32_t sm_off = live[u] ? m_base + (uint32_t)s * (4 * L::META_WORDS) : kOOB;
-            a[u] = bufA.ld16(sa_off);
-            idx[u] = bufM.ld4(sm_off) >> msh;
+        for (int u = 0; u < kGroup; ++u)
+            fa[u] = bufA.ld16(u < n_in ? a_base + (uint32_t)(s_first + u) * L::A_STEP_BYTES : kOOB);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const uint32_t o = live[u] ? b_base[mt] + (uint32_t)s * L::B_STEP_BYTES : kOOB;
-                b0[u][mt] = bufB.ld16(o + L::b_off0(kg));
-                b1[u][mt] = bufB.ld16(o + L::b_off1(kg));
-            }
+        for (int h = 0; h < M_LOADS; ++h) {
+            const int row = h * M_RPL + lane / M_CPR;
+            const int swz = M_CPR == 4 ? (row >> 2) & 3 : (row >> 1) & 7;
+            const uint32_t col = (uint32_t)g * M_ROW + 16 * ((lane % M_CPR) ^ swz);
+            const bool in = col < m_row_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufM.r, (lds_void*)(my_m + 1024 * h), 16,
+                                                     (int)(in ? (uint32_t)(a0 + row) * m_row_bytes + col : kOOB),
+                                                     0, 0, 0);
         }
+        uint4 xb0[kGroup][MT], xb1[kGroup][MT];
+        if (XLDS) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (live[u]) {
+            for (int j = 0; j < SL::XROWS; ++j) {
+                if (j >= RB)
+                    break;
+                const uint32_t col = (uint32_t)s_first * L::B_STEP_BYTES + 16 * lane;
+                const bool in = col < b_row_bytes;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(bufB.r, (lds_void*)(my_x + 1024 * j), 16,
+                                                         (int)(in ? (uint32_t)j * b_row_bytes + col : kOOB), 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint32_t o = u < n_in ? b_base[mt] + (uint32_t)(s_first + u) * L::B_STEP_BYTES : kOOB;
+                    xb0[u][mt] = bufB.ld16(o + L::b_off0(kg));
+                    xb1[u][mt] = bufB.ld16(o + L::b_off1(kg));
+                }
+        }
+        // ---- the group's loads (this wave's only) have landed
+        __builtin_amdgcn_s_waitcnt((0) | (0x7 << 4) | (0xF << 8));
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            if (u >= n_in)
+                break;
+            const int wbyte = 4 * (MWS * u + mwd);
+            const uint32_t idx = *reinterpret_cast<const uint32_t*>(
+                                     my_m + M_ROW * r + 16 * ((wbyte >> 4) ^ m_swz_r) + (wbyte & 15)) >> msh;
+            if (XLDS) {
+                const uint8_t* xr = r < RB ? my_x + 1024 * r + 128 * u : zero_pad;
+                const int o0 = r < RB ? L::b_off0(kg) : 0, o1 = r < RB ? L::b_off1(kg) : 0;
+                const uint4 b0 = *reinterpret_cast<const uint4*>(xr + o0);
+                const uint4 b1 = *reinterpret_cast<const uint4*>(xr + o1);
+                acc[0] = Op::mma(fa[u], b0, b1, idx, acc[0]);
+            } else {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    acc[mt] = Op::mma(a[u], b0[u][mt], b1[u][mt], idx[u], acc[mt]);
+                    acc[mt] = Op::mma(fa[u], xb0[u][mt], xb1[u][mt], idx, acc[mt]);
             }
         }
+        // the next group's DMA reuses this wave's LDS: finish reading it
+        __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
     }
 
 #pragma unroll
@@ -291,20 +357,26 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
     const int tiles16 = (RA + 15) / 16;
     if (RB <= 64) {
         const int steps = (int)(g.K / SparseOp<DT>::KSTEP);
-        // enough waves to cover the chip (>= ~8 per CU) without starving each wave of steps
-        int waves = 16;
-        while (waves > 4 && ((int64_t)tiles16 * waves > 8192 || steps < waves * 2))
+        const int groups = (steps + kGroup - 1) / kGroup;
+        // as many waves as there are load groups to split, up to 8 (measured
+        // best on every decode shape: more loads in flight per CU)
+        int waves = kMaxWaves;
+        while (waves > 2 && groups < waves)
             waves >>= 1;
-#define SP24_SKINNY(MT, U)                                                                            \
+#define SP24_SKINNY(MT, XL, NAME)                                                                     \
     do {                                                                                              \
-        hipLaunchKernelGGL((sp24_skinny<DT, OUT, MT, U>), dim3(tiles16), dim3(waves * 64), 0, s, av,    \
-                           g.a_meta, b, g.scale_a, g.scale_b, g.Y, RA, RB, g.K, sya, syb);            \
-        if (kname) *kname = "sp24_skinny_m" #MT;                                                      \
+        if (!g.dry)                                                                                   \
+            hipLaunchKernelGGL((sp24_skinny<DT, OUT, MT, XL>), dim3(tiles16), dim3(waves * 64), 0, s,   \
+                               av, g.a_meta, b, g.scale_a, g.scale_b, g.Y, RA, RB, g.K, sya, syb);    \
+        if (kname) *kname = NAME;                                                                     \
     } while (0)
+        // at most 4 dense rows: stage them through LDS with contiguous 1 KiB
+        // loads (a register load per step carries 64 useful bytes of 1 KiB)
         const int mt = (RB + 15) / 16;
-        if (mt <= 1) SP24_SKINNY(1, 4);
-        else if (mt == 2) SP24_SKINNY(2, 2);
-        else SP24_SKINNY(4, 2);
+        if (RB <= 4) SP24_SKINNY(1, true, "sp24_skinny_x4");
+        else if (mt <= 1) SP24_SKINNY(1, false, "sp24_skinny_m16");
+        else if (mt == 2) SP24_SKINNY(2, false, "sp24_skinny_m32");
+        else SP24_SKINNY(4, false, "sp24_skinny_m64");
 #undef SP24_SKINNY
     } else if ((int64_t)((RA + 255) / 256) * ((RB + 255) / 256) >= 192) {
         return launch_sp24_gemm_big(g, s, kname);
@@ -312,11 +384,12 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
         constexpr int FA = 4, FB = 4;
         using S = TiledShape<FA, FB>;
         const int tiles_a = (RA + S::BA - 1) / S::BA, tiles_b = (RB + S::BB - 1) / S::BB;
-        hipLaunchKernelGGL((sp24_tiled<DT, OUT, FA, FB>), dim3(tiles_a * tiles_b), dim3(256), 0, s, av,
-                           g.a_meta, b, g.scale_a, g.scale_b, g.Y, RA, RB, g.K, sya, syb, tiles_a);
+        if (!g.dry)
+            hipLaunchKernelGGL((sp24_tiled<DT, OUT, FA, FB>), dim3(tiles_a * tiles_b), dim3(256), 0, s, av,
+                               g.a_meta, b, g.scale_a, g.scale_b, g.Y, RA, RB, g.K, sya, syb, tiles_a);
         if (kname) *kname = "sp24_tiled_128x128";
     }
-    return hipGetLastError();
+    return g.dry ? hipSuccess : hipGetLastError();
 }
 
 }  // namespace

@@ -113,7 +113,10 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
         gm[j] = (uint32_t)(a0 + w / MWS) * m_row_bytes + 4 * (w % MWS);
     }
 
-    const int rot = (int)((blockIdx.x * 13u) % (unsigned)steps);
+    // K loop start rotated per group of tile-sharing workgroups: members of a
+    // group (resident together on one XCD) walk K in step and share operand
+    // slices through L2, while different groups spread over memory channels
+    const int rot = (int)(((unsigned)group * 13u) % (unsigned)steps);
     auto issue = [&](uint8_t* as, uint8_t* bs, uint8_t* ms, int sl) {
         // step sl of the rotated K loop; steps past the end load nothing useful
         int s = sl + rot;
@@ -224,11 +227,13 @@ hipError_t launch_big(const GemmArgs& g, hipStream_t s, const char** kname) {
     const int RB = (int)(g.a_is_w ? g.M : g.N);
     const int64_t sya = g.a_is_w ? 1 : g.N, syb = g.a_is_w ? g.N : 1;
     const int tiles_a = (RA + kBA - 1) / kBA, tiles_b = (RB + kBB - 1) / kBB;
+    if (kname)
+        *kname = "sp24_big_256x256";
+    if (g.dry)
+        return hipSuccess;
     hipLaunchKernelGGL((sp24_big<DT, OUT>), dim3(tiles_a * tiles_b), dim3(kThreads), 0, s,
                        (const uint8_t*)g.a_vals, g.a_meta, (const uint8_t*)g.b, g.scale_a, g.scale_b, g.Y, RA,
                        RB, g.K, sya, syb, tiles_a, tiles_b);
-    if (kname)
-        *kname = "sp24_big_256x256";
     return hipGetLastError();
 }
 

@@ -44,8 +44,10 @@ struct GemmArgs {
     const float* scale_b;    // per dense-operand row, or null
     void* Y;                 // M x N
     int a_is_w;              // 1: compressed operand is W (rows = N), 0: it is X (rows = M)
+    bool dry = false;        // only report the kernel that would be launched
 };
-// Sparse GEMM; writes the name of the kernel it launched into kname (if non-null).
+// Sparse GEMM; writes the name of the kernel it launched into kname (if
+// non-null).  With g.dry set, launches nothing and returns hipSuccess.
 hipError_t launch_sp24_gemm(const GemmArgs& g, hipStream_t s, const char** kname);
 // The 256 x 256-tile sparse kernel for large M (called by launch_sp24_gemm).
 hipError_t launch_sp24_gemm_big(const GemmArgs& g, hipStream_t s, const char** kname);
@@ -58,7 +60,10 @@ struct DenseArgs {
     const float* scale_x;
     const float* scale_w;
     void* Y;
+    bool dry = false;        // only report the kernel that would be launched
 };
 hipError_t launch_dense_gemm(const DenseArgs& g, hipStream_t s, const char** kname);
+// The 256 x 256-tile dense kernel for large M (called by launch_dense_gemm).
+hipError_t launch_dense_gemm_big(const DenseArgs& g, hipStream_t s, const char** kname);
 
 }  // namespace sp24

@@ -97,6 +97,28 @@ def test_select_tactic_validation():
              ctypes.byref(rec)) == 1
 
 
+def test_gemm_kernel_names_follow_the_dispatch():
+    bf = __import__("torch").bfloat16
+    k = sp.gemm_kernel
+    # decode: one to four dense rows are staged through LDS, up to 64 go through registers
+    assert k(True, sp.SPARSE_W, bf, bf, 1, 4096, 4096) == "sp24_skinny_x4"
+    assert k(True, sp.SPARSE_W, bf, bf, 4, 4096, 4096) == "sp24_skinny_x4"
+    assert k(True, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "sp24_skinny_m16"
+    assert k(True, sp.SPARSE_W, bf, bf, 64, 4096, 4096) == "sp24_skinny_m64"
+    assert k(False, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "dense_skinny_m1"
+    # large outputs take the 256 x 256 tiles once they fill the chip (192 tiles)
+    assert k(True, sp.SPARSE_W, bf, bf, 8192, 4096, 4096) == "sp24_big_256x256"
+    assert k(False, sp.SPARSE_W, bf, bf, 8192, 4096, 4096) == "dense_big_256x256"
+    assert k(True, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "sp24_tiled_128x128"
+    # rejected shapes and degenerate ones
+    assert k(True, sp.SPARSE_W, bf, bf, 4, 4096, 96) is None
+    assert k(False, sp.SPARSE_W, bf, bf, 4, 4096, 100) is None
+    assert k(False, sp.SPARSE_W, bf, bf, 4, 4096, 104) == "dense_skinny_m1"
+    assert k(True, sp.SPARSE_W, bf, bf, 0, 4096, 128) == "none"
+    assert k(True, sp.SPARSE_W, bf, bf, 4, 4096, 0) == "fill_zero"
+    assert k(True, 5, bf, bf, 4, 4096, 128) is None
+
+
 # ------------------------------------------------------------ decision rule
 
 def test_decide_sparse_strictly_faster():

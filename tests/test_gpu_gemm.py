@@ -147,6 +147,37 @@ def test_dense_accepts_k_the_sparse_path_rejects(dt, M, N, K):
     assert np.array_equal(Y, R)
 
 
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
+@pytest.mark.parametrize("which", ["sparse_w", "sparse_x", "dense"])
+def test_large_tile_kernels_ragged(dt, which):
+    """Shapes with >= 192 tiles of 256 x 256 run the large-tile kernels; these
+    have ragged last tiles in both dimensions (and, for dense, a partial last
+    K step).  Integer inputs: sampled rows must match the oracle exactly."""
+    M, N = 3000, 4100
+    K = 384 if dt != oracle.E4M3 else 512
+    if which == "dense":
+        K += 16                     # not a whole 64-K (128-K) step
+    say("large ragged", which, dt, M, N, K)
+    xb, _, wb, _ = _operands(dt, M, N, K, 123, integer=True)
+    rows = np.array([0, 1, 255, 256, 1777, 2999])
+    X, W = to_dev(xb, dt), to_dev(wb, dt)
+    if which == "sparse_w":
+        wv, wm = oracle.prune_compress(dt, wb)
+        R = oracle.gemm(dt, M, N, K, x=xb, w_vals=wv, w_meta=wm, mrows=rows)
+        v, m = sp.prune_compress(W)
+        Y = sp.sp24_gemm(sp.SPARSE_W, v, m, X, M, N, K, out_dtype=torch.float32)
+    elif which == "sparse_x":
+        xv, xm = oracle.prune_compress(dt, xb)
+        R = oracle.gemm(dt, M, N, K, x_vals=xv, x_meta=xm, w=wb, mrows=rows)
+        v, m = sp.prune_compress(X)
+        Y = sp.sp24_gemm(sp.SPARSE_X, v, m, W, M, N, K, out_dtype=torch.float32)
+    else:
+        R = oracle.gemm(dt, M, N, K, x=xb, w=wb, mrows=rows)
+        Y = sp.dense_gemm(X, W, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(decode_out(Y[torch.from_numpy(rows).cuda()]), R)
+
+
 def test_one_hot_rows_read_back_weights():
     """X = identity rows: Y[m, :] is column m of the decompressed W, which
     checks every metadata position and word through the sparse MMA."""
