@@ -6,11 +6,14 @@ A step is one pass of the whole hot path over the workload's synthetic,
 seeded operands: for every weight shape, prune+compress the weight (or, for
 the online workload, the activation), decompress it (the dense pruned weight
 the fallback uses), then for every M the sparse GEMM and the dense GEMM on
-the same shapes.  Every kernel is timed with HIP events on the stream it runs
-on; HBM-bound kernels run "cold" (an untimed read of a 1 GiB buffer before
-each evicts L2 and the 256 MB Infinity Cache), compute-bound ones "warm".
-After the timed steps the per-shape tactic (sparse iff faster) is selected
-and the CPU oracle is timed on the host cores.  Rank 0 prints one JSON line.
+the same shapes.  Each of these runs as a chain of launches (about 1.5 ms of
+work) captured in a HIP graph and timed with HIP events on the stream it runs
+on (time per launch = chain time / launches).  HBM-bound workloads run "cold": the launches of a
+chain cycle through copies of the weights totalling 640 MiB, so every launch
+reads its operands from HBM as successive layers do; compute-bound ones run
+warm on one copy.  After the timed steps the per-shape tactic (sparse iff
+faster) is selected and the CPU oracle is timed on the host cores.  One JSON
+line is printed.
 
 Workloads (default: decode, the bf16 Llama-3-8B-like decode layers):
   tiny | decode | prefill | fp8 | online
@@ -84,47 +87,57 @@ def traffic_per_launch(kernel, workload):
     return None
 
 
-class Timer:
-    """HIP events on torch's current stream (the one the library launches on)."""
-
-    def __init__(self):
-        self.pending = []           # (key, start, end)
-
-    def time(self, key, fn):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        self.pending.append((key, a, b))
-
-    def collect(self):
-        torch.cuda.synchronize()
-        out = {}
-        for key, a, b in self.pending:
-            out.setdefault(key, []).append(a.elapsed_time(b) * 1e3)   # microseconds
-        self.pending = []
-        return out
+# Cold protocol for HBM-bound kernels: consecutive launches of a chain cycle through this many bytes
+# of distinct operand copies, more than twice the 32 MB of L2 plus the 256 MB Infinity Cache, so that
+# every launch reads its weights from HBM -- as the layers of a decode step do.  Warm kernels re-run
+# on one copy.
+COLD_BYTES = 640 << 20
+MAX_COPIES = 64
+# A chain runs for about this long, so that the fixed cost of starting a graph (~20 us) stays a
+# small part of the bracketed time.
+CHAIN_US = 1500.0
 
 
-def build_cases(workload):
+def chain_length(est_us, copies):
+    """Launches in a chain: about CHAIN_US of work, at least 8, a whole number of passes over the copies."""
+    n = int(min(1024, max(8, -(-CHAIN_US // max(est_us, 1.0)))))
+    return -(-n // copies) * copies
+
+
+def est_us(nbytes, flops):
+    """Rough duration of one launch (4 TB/s, 1 PFLOP/s, 2 us fixed) used only to size chains."""
+    return max(nbytes / 4e6, flops / 1e9) + 2.0
+
+
+def n_copies(compressed_bytes, cold):
+    if not cold:
+        return 1
+    return int(min(MAX_COPIES, max(2, -(-COLD_BYTES // compressed_bytes))))
+
+
+def build_cases(workload, cold):
     w = inputs.WORKLOADS[workload]
     dt, out = w["dtype"], w["out"]
+    eb = inputs.ELEM_BYTES[dt]
+    ytype = TORCH[out] if out in TORCH else torch.float32
     cases = []
     for s, (N, K) in enumerate(w["shapes"]):
         wb, sw = inputs.weight(workload, s)
-        W = dev(wb, dt)
-        shape = {"s": s, "N": N, "K": K, "W": W,
-                 "sw": None if sw is None else torch.from_numpy(sw).cuda(), "ms": []}
-        v, m = sp.prune_compress(W)
-        shape["v"], shape["m"] = v, m
-        shape["Wp"] = sp.decompress(v, m, K)
+        W0 = dev(wb, dt)
+        shape = {"s": s, "N": N, "K": K, "sw": None if sw is None else torch.from_numpy(sw).cuda(), "ms": []}
+        nc = 1 if workload == "online" else n_copies(N * K * eb // 2 + N * K // 8, cold)
+        copies = []
+        for i in range(nc):
+            W = W0 if i == 0 else W0.clone()
+            v, m = sp.prune_compress(W)
+            copies.append({"W": W, "v": v, "m": m, "Wp": sp.decompress(v, m, K)})
+        shape["copies"] = copies
         for j, M in enumerate(w["ms"]):
             xb, sx = inputs.activation(workload, s, j)
             X = dev(xb, dt)
             item = {"j": j, "M": M, "X": X, "sx": None if sx is None else torch.from_numpy(sx).cuda(),
-                    "Y": torch.empty((M, N), dtype=TORCH[out] if out in TORCH else torch.float32, device="cuda"),
-                    "Yd": torch.empty((M, N), dtype=TORCH[out] if out in TORCH else torch.float32, device="cuda")}
+                    "Y": torch.empty((M, N), dtype=ytype, device="cuda"),
+                    "Yd": torch.empty((M, N), dtype=ytype, device="cuda")}
             if workload == "online":
                 item["xv"] = torch.empty((M, K // 2), dtype=TORCH[dt], device="cuda")
                 item["xm"] = torch.empty((M, (K + 31) // 32), dtype=torch.int32, device="cuda")
@@ -134,77 +147,129 @@ def build_cases(workload):
     return cases
 
 
-def run_step(workload, cases, timer, flush, cold):
+def chains(workload, cases):
+    """The step as an ordered list of (key, launches, fn): fn(i) issues launch i of the chain."""
     w = inputs.WORKLOADS[workload]
-    dt = w["dtype"]
+    eb = inputs.ELEM_BYTES[w["dtype"]]
+    out = []
     for c in cases:
-        N, K = c["N"], c["K"]
+        N, K, cp = c["N"], c["K"], c["copies"]
+        nc = len(cp)
+        pick = lambda i, cp=cp: cp[i % len(cp)]
         if workload != "online":
-            if cold:
-                flush.sum()
-            timer.time(("compress", c["s"]), lambda: sp.prune_compress(c["W"], values=c["v"], meta=c["m"]))
-            if cold:
-                flush.sum()
-            timer.time(("decompress", c["s"]), lambda: sp.decompress(c["v"], c["m"], K, out=c["Wp"]))
+            L = chain_length(est_us(N * K * eb * 1.625, 0), nc)
+            out.append((("compress", c["s"]), L,
+                        lambda i, pick=pick: sp.prune_compress(pick(i)["W"], values=pick(i)["v"], meta=pick(i)["m"])))
+            out.append((("decompress", c["s"]), L,
+                        lambda i, pick=pick, K=K: sp.decompress(pick(i)["v"], pick(i)["m"], K, out=pick(i)["Wp"])))
         for it in c["ms"]:
-            M = it["M"]
+            M, key = it["M"], (c["s"], it["j"])
+            L = chain_length(est_us((N * K + M * K) * eb, 2.0 * M * N * K), nc)
             if workload == "online":
                 # the activation is the sparse operand: prune+compress it on every call
-                timer.time(("compress", c["s"], it["j"]),
-                           lambda: sp.prune_compress(it["X"], values=it["xv"], meta=it["xm"]))
-                timer.time(("sparse", c["s"], it["j"]),
-                           lambda: sp.sp24_gemm(sp.SPARSE_X, it["xv"], it["xm"], c["W"], M, N, K, out=it["Y"]))
-                timer.time(("dense", c["s"], it["j"]), lambda: sp.dense_gemm(it["X"], c["W"], out=it["Yd"]))
+                W = cp[0]["W"]
+                out.append((("compress",) + key, chain_length(est_us(M * K * eb * 1.625, 0), 1),
+                            lambda i, it=it: sp.prune_compress(it["X"], values=it["xv"], meta=it["xm"])))
+                out.append((("sparse",) + key, L,
+                            lambda i, it=it, W=W, M=M, N=N, K=K:
+                            sp.sp24_gemm(sp.SPARSE_X, it["xv"], it["xm"], W, M, N, K, out=it["Y"])))
+                out.append((("dense",) + key, L, lambda i, it=it, W=W: sp.dense_gemm(it["X"], W, out=it["Yd"])))
                 continue
-            if cold:
-                flush.sum()
-            timer.time(("sparse", c["s"], it["j"]),
-                       lambda: sp.sp24_gemm(sp.SPARSE_W, c["v"], c["m"], it["X"], M, N, K,
-                                            scale_x=it["sx"], scale_w=c["sw"], out=it["Y"]))
-            if cold:
-                flush.sum()
-            timer.time(("dense", c["s"], it["j"]),
-                       lambda: sp.dense_gemm(it["X"], c["Wp"], scale_x=it["sx"], scale_w=c["sw"], out=it["Yd"]))
+            out.append((("sparse",) + key, L,
+                        lambda i, it=it, pick=pick, M=M, N=N, K=K, c=c:
+                        sp.sp24_gemm(sp.SPARSE_W, pick(i)["v"], pick(i)["m"], it["X"], M, N, K,
+                                     scale_x=it["sx"], scale_w=c["sw"], out=it["Y"])))
+            out.append((("dense",) + key, L,
+                        lambda i, it=it, pick=pick, c=c:
+                        sp.dense_gemm(it["X"], pick(i)["Wp"], scale_x=it["sx"], scale_w=c["sw"], out=it["Yd"])))
+    return out
+
+
+class Runner:
+    """Each chain is captured once in a HIP graph (so launches follow each other with no host gap)
+    and replayed between two HIP events on the stream it was captured for; the per-launch time is
+    the bracketed time over the chain's length."""
+
+    def __init__(self, items):
+        self.items = items
+        for _, n, fn in items:          # eager pass: loads every code object before capture
+            for i in range(n):
+                fn(i)
+        torch.cuda.synchronize()
+        self.length = {key: n for key, n, _ in items}
+        self.graphs = []
+        for _, n, fn in items:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    fn(i)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+        self.pending = []
+
+    def step(self):
+        for (key, n, _), g in zip(self.items, self.graphs):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            self.pending.append((key, n, a, b))
+
+    def collect(self):
+        torch.cuda.synchronize()
+        out = {}
+        for key, n, a, b in self.pending:
+            out.setdefault(key, []).append(a.elapsed_time(b) * 1e3 / n)   # microseconds per launch
+        self.pending = []
+        return out
 
 
 def cpu_baseline(workload, budget_s):
     """The oracle as it stands, on the host cores, over a bounded sample of the
-    same workload: its GEMMs (fp64 on the decompressed weight) for as many
-    (shape, M) cases as fit the time budget, rows of M sampled when M is large."""
+    same workload: its GEMMs (fp64 on the decompressed weight) over the
+    workload's (shape, M) cases, rows of M sampled when M is large, passes over
+    the cases repeated until about budget_s seconds of GEMM time are spent."""
     import oracle
 
     w = inputs.WORKLOADS[workload]
     dt = w["dtype"]
-    flops = 0.0
-    secs = 0.0
-    done = []
-    t_start = time.perf_counter()
+    prepared = []
     for s, (N, K) in enumerate(w["shapes"]):
-        if secs > budget_s or time.perf_counter() - t_start > 3 * budget_s:
-            break
         wb, sw = inputs.weight(workload, s)
+        wv = wm = None
         if workload != "online":
             wv, wm = oracle.prune_compress(dt, wb)
         for j, M in enumerate(w["ms"]):
-            if secs > budget_s or time.perf_counter() - t_start > 3 * budget_s:
-                break
             xb, sx = inputs.activation(workload, s, j)
             rows = M if M <= 64 else 16
             mrows = np.linspace(0, M - 1, rows).astype(np.int64)
+            xv = xm = None
             if workload == "online":
                 xv, xm = oracle.prune_compress(dt, xb)
-                t0 = time.perf_counter()
+            prepared.append((N, K, M, rows, mrows, wb, sw, wv, wm, xb, sx, xv, xm))
+    flops = 0.0
+    secs = 0.0
+    calls = 0
+    names = []
+    while secs < budget_s:
+        for (N, K, M, rows, mrows, wb, sw, wv, wm, xb, sx, xv, xm) in prepared:
+            t0 = time.perf_counter()
+            if workload == "online":
                 oracle.gemm(dt, M, N, K, x_vals=xv, x_meta=xm, w=wb, mrows=mrows)
             else:
-                t0 = time.perf_counter()
                 oracle.gemm(dt, M, N, K, x=xb, w_vals=wv, w_meta=wm, scale_x=sx, scale_w=sw, mrows=mrows)
             secs += time.perf_counter() - t0
             flops += 2.0 * rows * N * K
-            done.append(f"({N},{K})xM{M}" + ("" if rows == M else f"[{rows} rows]"))
+            calls += 1
+            if len(names) < len(prepared):
+                names.append(f"({N},{K})xM{M}" + ("" if rows == M else f"[{rows} rows]"))
+            if secs >= budget_s:
+                break
     return {"value": flops / secs / 1e12 if secs > 0 else None, "unit": "TFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"oracle fp64 GEMM on the decompressed operand, {len(done)} cases: " + " ".join(done) +
-                      f"; {secs:.1f} s of GEMM time"}
+            "sample": f"oracle fp64 GEMM on the decompressed operand over the cases " + " ".join(names) +
+                      f": {calls} calls, {secs:.1f} s of GEMM time"}
 
 
 def main():
@@ -237,28 +302,28 @@ def main():
     cold = (workload in ("decode", "fp8", "tiny")) if args.cold == "auto" else args.cold == "on"
     scales = dt == inputs.E4M3
 
-    cases = build_cases(workload)
-    # cold runs read (not write) a 1 GiB buffer before each timed kernel: that evicts L2 and the
-    # 256 MB Infinity Cache without leaving dirty lines whose write-back would compete with the kernel
-    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda") if cold else None
-    timer = Timer()
+    cases = build_cases(workload, cold)
+    runner = Runner(chains(workload, cases))
     for _ in range(args.warmup):
-        run_step(workload, cases, timer, flush, cold)
-    timer.collect()
+        runner.step()
+    runner.collect()
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_step(workload, cases, timer, flush, cold)
+        runner.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    times = timer.collect()
+    times = runner.collect()
 
     if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda")
-        b = torch.empty(n, dtype=torch.uint8, device="cuda")
-        b.copy_(a)
+        # a kernel that reads and writes exactly this many bytes (an elementwise negation, which
+        # a DMA engine cannot take over as it may a plain copy): the yardstick for the byte counters
+        n = args.copy_calibration_mib << 18
+        a = torch.ones(n, dtype=torch.int32, device="cuda")
+        b = torch.empty(n, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)
         torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- per-case table
@@ -314,13 +379,15 @@ def main():
             M, N, K = it["M"], c["N"], c["K"]
             which = sp.SPARSE_X if workload == "online" else sp.SPARSE_W
             name = sp.gemm_kernel(True, which, TORCH[dt], it["Y"].dtype, M, N, K)
-            ts = times[("sparse", c["s"], it["j"])]
+            key = ("sparse", c["s"], it["j"])
+            ts, L = times[key], runner.length[key]       # per-launch means of each step; chain length
             sparse_rows = M if workload == "online" else N
             k = per_kernel.setdefault(name, {"t": 0.0, "n": 0, "bytes": 0.0, "flops": 0.0})
-            k["t"] += sum(ts)
-            k["n"] += len(ts)
-            k["bytes"] += sparse_gemm_bytes(M, N, K, eb, out_eb, sparse_rows, scales) * len(ts)
-            k["flops"] += 2.0 * M * N * K * len(ts)
+            # weighted by launches, as a profiler's per-kernel average is
+            k["t"] += sum(ts) * L
+            k["n"] += len(ts) * L
+            k["bytes"] += sparse_gemm_bytes(M, N, K, eb, out_eb, sparse_rows, scales) * len(ts) * L
+            k["flops"] += 2.0 * M * N * K * len(ts) * L
     kname = max(per_kernel, key=lambda n: per_kernel[n]["t"])
     k = per_kernel[kname]
     avg_us = k["t"] / k["n"]
@@ -339,8 +406,9 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic_per_launch(kname, workload),
                 "kernel": kname, "launches": k["n"], "flops_per_launch": round(k["flops"] / k["n"]),
                 "avg_launch_us": round(avg_us, 3)}
+    all_t = sum(v["t"] for v in per_kernel.values())
     roof["kernels"] = {n: {"launches": v["n"], "avg_launch_us": round(v["t"] / v["n"], 3),
-                           "share": round(v["t"] / tot["sparse_t"], 3)} for n, v in per_kernel.items()}
+                           "share": round(v["t"] / all_t, 3)} for n, v in per_kernel.items()}
 
     tactics = []
     if not args.no_tactic:
@@ -348,10 +416,10 @@ def main():
             for it in c["ms"]:
                 M, N, K = it["M"], c["N"], c["K"]
                 if workload == "online":
-                    rec = sp.select_tactic(sp.SPARSE_X, it["xv"], it["xm"], c["W"], it["X"], M, N, K,
+                    rec = sp.select_tactic(sp.SPARSE_X, it["xv"], it["xm"], c["copies"][0]["W"], it["X"], M, N, K,
                                            y_scratch=it["Y"], warmup=3, reps=10)
                 else:
-                    rec = sp.select_tactic(sp.SPARSE_W, c["v"], c["m"], it["X"], c["Wp"], M, N, K,
+                    rec = sp.select_tactic(sp.SPARSE_W, c["copies"][0]["v"], c["copies"][0]["m"], it["X"], c["copies"][0]["Wp"], M, N, K,
                                            scale_x=it["sx"], scale_w=c["sw"], y_scratch=it["Y"], warmup=3,
                                            reps=10)
                 tactics.append({"N": N, "K": K, "M": M, "selected": rec["selected"], "ratio": round(rec["ratio"], 3),
@@ -368,7 +436,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[dt], "data": "synthetic",
         "config": {"workload": workload, "shapes_NK": w["shapes"], "M": w["ms"], "dtype": DTYPE_NAME[dt],
                    "out_dtype": "f32" if out == inputs.F32 else DTYPE_NAME[out],
-                   "cache": "cold (1 GiB read before each kernel)" if cold else "warm",
+                   "cache": "cold (launches cycle through 640 MiB of weight copies)" if cold else "warm",
                    "seeds": "10000*c + 100*s + 10*t + j"},
         "speedup_vs_dense": round(speedup, 3),
         "compress_GBps": round(compress_gbps, 1),

@@ -11,11 +11,11 @@
 //
 // Two kernels:
 //   skinny  few B rows (decode: M <= 64).  HBM-bound on the compressed
-//           weight.  One workgroup owns 16 rows of A and all of B; its waves
-//           split K (step s goes to wave s % waves), load operands straight
-//           from global memory into registers (16-byte loads, each row's
-//           bytes read once), and reduce their partial tiles through LDS in
-//           a fixed order (deterministic, no atomics).
+//           weight.  One workgroup owns 16 (or 32) rows of A and all of B;
+//           its waves split K into runs of 8-step groups, issue every load
+//           of a group at once (A into registers, metadata and up to 4 B rows
+//           into LDS by direct global->LDS loads), and reduce their partial
+//           tiles through LDS in a fixed order (deterministic, no atomics).
 //   tiled   large M (prefill, dynamic operands).  Workgroup tile BA x BB,
 //           K staged through double-buffered LDS one instruction step at a
 //           time, 2 x 2 waves each owning (FA x FB) 16x16 fragments.
@@ -30,18 +30,24 @@ constexpr int kGroup = 8;   // K-steps per load group
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Per wave and load group: the group's metadata of the 16 rows (1 KiB for
-// 16-bit steps, 2 KiB for fp8) and, for at most 4 dense rows, the group's
-// slice of those rows (4 x 1 KiB) plus a zero pad read by the empty lanes.
-template <int MWS>
+// Per wave and load group: the group's metadata of the 16 * AT rows (1 KiB
+// per 16 rows for 16-bit steps, 2 KiB for fp8) and, for at most 4 dense rows,
+// the group's slice of those rows (4 x 1 KiB) plus a zero pad read by the
+// empty lanes.
+template <int MWS, int AT>
 struct SkinnyLds {
-    static constexpr int META = 16 * kGroup * MWS * 4;
+    static constexpr int META = 16 * AT * kGroup * MWS * 4;
     static constexpr int XROWS = 4;
     static constexpr int X = XROWS * kGroup * 128;
     static constexpr int PER_WAVE = META + X + 32;
 };
 
-template <sp24_dtype DT, sp24_dtype OUT, int MT, bool XLDS>
+// AT: 16-row A tiles per workgroup (2 halves the B traffic per A byte when
+// there are enough tiles to fill the chip); MT: 16-column B fragments held in
+// registers at once; PASSES: passes over the group with MT fragments each
+// (the A registers are reused; B in registers for a whole group costs
+// 8 steps x MT x 32 bytes per lane).
+template <sp24_dtype DT, sp24_dtype OUT, int MT, bool XLDS, int AT, int PASSES>
 __global__ void __launch_bounds__(kMaxWaves * 64, 2)
 sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
             const uint8_t* __restrict__ B, const float* __restrict__ sa, const float* __restrict__ sb,
@@ -49,19 +55,20 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
     using L = StepLayout<DT>;
     using Op = SparseOp<DT>;
     constexpr int MWS = L::META_WORDS;
-    using SL = SkinnyLds<MWS>;
+    using SL = SkinnyLds<MWS, AT>;
     constexpr int M_ROW = kGroup * MWS * 4;         // metadata bytes of one row per group: 64 or 128
     constexpr int M_CPR = M_ROW / 16;               // 16-byte chunks per row: 4 or 8
-    constexpr int M_LOADS = SL::META / 1024;        // 1 or 2
+    constexpr int M_LOADS = SL::META / 1024;        // AT or 2 * AT
     constexpr int M_RPL = 1024 / M_ROW;             // rows per load: 16 or 8
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kMaxWaves][SL::PER_WAVE];
-    __shared__ float red[kMaxWaves][MT][4][64];
+    constexpr int MTT = MT * PASSES;                // B fragments in all
+    __shared__ float red[kMaxWaves][AT][MTT][4][64];
 
     const int WAVES = blockDim.x >> 6;   // the waves split K
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, kg = lane >> 4;
-    const int a0 = blockIdx.x * 16;
+    const int a0 = blockIdx.x * 16 * AT;
     const int steps = (int)(K / L::KSTEP);
     const int groups = (steps + kGroup - 1) / kGroup;
     const uint32_t a_row_bytes = (uint32_t)(K / 2 * L::ELEM), b_row_bytes = (uint32_t)(K * L::ELEM);
@@ -75,21 +82,26 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
     if (XLDS && lane < 8)
         reinterpret_cast<uint32_t*>(zero_pad)[lane] = 0u;
 
-    // A: straight from HBM into the operand registers, one 1 KiB load per step
-    const uint32_t a_base = (uint32_t)(a0 + r) * a_row_bytes + L::a_off(kg);
+    // A: straight from HBM into the operand registers, one 1 KiB load per step and tile
+    uint32_t a_base[AT];
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+        a_base[t] = (uint32_t)(a0 + 16 * t + r) * a_row_bytes + L::a_off(kg);
     // metadata: DMA lane roles (row, chunk slot), chunks XOR-swizzled by row
     const int m_swz_r = M_CPR == 4 ? (r >> 2) & 3 : (r >> 1) & 7;
     const int msh = L::meta_shift(kg), mwd = L::meta_word(kg);
     // X through registers (more than 4 dense rows) or through LDS (at most 4)
-    uint32_t b_base[MT];
+    uint32_t b_base[MTT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MTT; ++mt)
         b_base[mt] = (uint32_t)(mt * 16 + r) * b_row_bytes;
 
-    f32x4 acc[MT];
+    f32x4 acc[AT][MTT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < AT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MTT; ++mt)
+            acc[t][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     // each wave streams a contiguous run of groups; the run of the whole
     // workgroup starts at a rotated group so that concurrent workgroups read
@@ -104,10 +116,12 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
         const int s_first = g * kGroup;
         const int n_in = min(kGroup, steps - s_first);
         // ---- issue: A for the group's steps, metadata and X by DMA
-        uint4 fa[kGroup];
+        uint4 fa[AT][kGroup];
 #pragma unroll
-        for (int u = 0; u < kGroup; ++u)
-            fa[u] = bufA.ld16(u < n_in ? a_base + (uint32_t)(s_first + u) * L::A_STEP_BYTES : kOOB);
+        for (int t = 0; t < AT; ++t)
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u)
+                fa[t][u] = bufA.ld16(u < n_in ? a_base[t] + (uint32_t)(s_first + u) * L::A_STEP_BYTES : kOOB);
 #pragma unroll
         for (int h = 0; h < M_LOADS; ++h) {
             const int row = h * M_RPL + lane / M_CPR;
@@ -118,7 +132,6 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
                                                      (int)(in ? (uint32_t)(a0 + row) * m_row_bytes + col : kOOB),
                                                      0, 0, 0);
         }
-        uint4 xb0[kGroup][MT], xb1[kGroup][MT];
         if (XLDS) {
 #pragma unroll
             for (int j = 0; j < SL::XROWS; ++j) {
@@ -129,35 +142,50 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(bufB.r, (lds_void*)(my_x + 1024 * j), 16,
                                                          (int)(in ? (uint32_t)j * b_row_bytes + col : kOOB), 0, 0, 0);
             }
-        } else {
-#pragma unroll
-            for (int u = 0; u < kGroup; ++u)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const uint32_t o = u < n_in ? b_base[mt] + (uint32_t)(s_first + u) * L::B_STEP_BYTES : kOOB;
-                    xb0[u][mt] = bufB.ld16(o + L::b_off0(kg));
-                    xb1[u][mt] = bufB.ld16(o + L::b_off1(kg));
-                }
         }
-        // ---- the group's loads (this wave's only) have landed
-        __builtin_amdgcn_s_waitcnt((0) | (0x7 << 4) | (0xF << 8));
 #pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            if (u >= n_in)
-                break;
-            const int wbyte = 4 * (MWS * u + mwd);
-            const uint32_t idx = *reinterpret_cast<const uint32_t*>(
-                                     my_m + M_ROW * r + 16 * ((wbyte >> 4) ^ m_swz_r) + (wbyte & 15)) >> msh;
-            if (XLDS) {
-                const uint8_t* xr = r < RB ? my_x + 1024 * r + 128 * u : zero_pad;
-                const int o0 = r < RB ? L::b_off0(kg) : 0, o1 = r < RB ? L::b_off1(kg) : 0;
-                const uint4 b0 = *reinterpret_cast<const uint4*>(xr + o0);
-                const uint4 b1 = *reinterpret_cast<const uint4*>(xr + o1);
-                acc[0] = Op::mma(fa[u], b0, b1, idx, acc[0]);
-            } else {
+        for (int p = 0; p < PASSES; ++p) {
+            uint4 xb0[kGroup][MT], xb1[kGroup][MT];
+            if (!XLDS) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[mt] = Op::mma(fa[u], xb0[u][mt], xb1[u][mt], idx, acc[mt]);
+                for (int u = 0; u < kGroup; ++u)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const uint32_t o = u < n_in ? b_base[p * MT + mt] + (uint32_t)(s_first + u) * L::B_STEP_BYTES
+                                                    : kOOB;
+                        xb0[u][mt] = bufB.ld16(o + L::b_off0(kg));
+                        xb1[u][mt] = bufB.ld16(o + L::b_off1(kg));
+                    }
+            }
+            // ---- the pass's loads (this wave's only) have landed
+            __builtin_amdgcn_s_waitcnt((0) | (0x7 << 4) | (0xF << 8));
+            // steps past the end of K (last group only) were loaded as zeros
+            // and add nothing; running them keeps every load of the group used
+            // unconditionally, which keeps the compiler from sinking each load
+            // next to its use (one memory round trip per step)
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const int wbyte = 4 * (MWS * u + mwd);
+                uint32_t idx[AT];
+#pragma unroll
+                for (int t = 0; t < AT; ++t)
+                    idx[t] = *reinterpret_cast<const uint32_t*>(my_m + M_ROW * (16 * t + r) +
+                                                                16 * ((wbyte >> 4) ^ m_swz_r) + (wbyte & 15)) >> msh;
+                if (XLDS) {
+                    const uint8_t* xr = r < RB ? my_x + 1024 * r + 128 * u : zero_pad;
+                    const int o0 = r < RB ? L::b_off0(kg) : 0, o1 = r < RB ? L::b_off1(kg) : 0;
+                    const uint4 b0 = *reinterpret_cast<const uint4*>(xr + o0);
+                    const uint4 b1 = *reinterpret_cast<const uint4*>(xr + o1);
+#pragma unroll
+                    for (int t = 0; t < AT; ++t)
+                        acc[t][0] = Op::mma(fa[t][u], b0, b1, idx[t], acc[t][0]);
+                } else {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int t = 0; t < AT; ++t)
+                            acc[t][p * MT + mt] = Op::mma(fa[t][u], xb0[u][mt], xb1[u][mt], idx[t], acc[t][p * MT + mt]);
+                }
             }
         }
         // the next group's DMA reuses this wave's LDS: finish reading it
@@ -165,20 +193,24 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
     }
 
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < AT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            red[wave][mt][i][lane] = acc[mt][i];
+        for (int mt = 0; mt < MTT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                red[wave][t][mt][i][lane] = acc[t][mt][i];
     __syncthreads();
 
-    // D[4*kg + i][l % 16] of fragment mt lives at red[.][mt][i][kg*16 + l%16]
-    for (int o = threadIdx.x; o < 16 * 16 * MT; o += WAVES * 64) {
-        const int al = o & 15, bl = o >> 4;
+    // D[4*kg + i][l % 16] of fragment (t, mt) lives at red[.][t][mt][i][kg*16 + l%16]
+    constexpr int TILE = 16 * 16 * MTT;
+    for (int o = threadIdx.x; o < AT * TILE; o += WAVES * 64) {
+        const int t = o / TILE, ot = o - t * TILE;
+        const int al = ot & 15, bl = ot >> 4;
         const int mt = bl >> 4, ln = ((al >> 2) << 4) | (bl & 15), i = al & 3;
         float v = 0.f;
         for (int w = 0; w < WAVES; ++w)   // fixed order: deterministic
-            v += red[w][mt][i][ln];
-        const int ar = a0 + al, br = bl;
+            v += red[w][t][mt][i][ln];
+        const int ar = a0 + 16 * t + al, br = bl;
         if (ar < RA && br < RB) {
             if (sa)
                 v *= sa[ar];
@@ -363,20 +395,29 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
         int waves = kMaxWaves;
         while (waves > 2 && groups < waves)
             waves >>= 1;
-#define SP24_SKINNY(MT, XL, NAME)                                                                     \
+#define SP24_SKINNY(MT, XL, AT, P, NAME)                                                              \
     do {                                                                                              \
         if (!g.dry)                                                                                   \
-            hipLaunchKernelGGL((sp24_skinny<DT, OUT, MT, XL>), dim3(tiles16), dim3(waves * 64), 0, s,   \
-                               av, g.a_meta, b, g.scale_a, g.scale_b, g.Y, RA, RB, g.K, sya, syb);    \
+            hipLaunchKernelGGL((sp24_skinny<DT, OUT, MT, XL, AT, P>), dim3((RA + 16 * AT - 1) / (16 * AT)), \
+                               dim3(waves * 64), 0, s, av, g.a_meta, b, g.scale_a, g.scale_b, g.Y, RA, RB, \
+                               g.K, sya, syb);                                                        \
         if (kname) *kname = NAME;                                                                     \
     } while (0)
         // at most 4 dense rows: stage them through LDS with contiguous 1 KiB
-        // loads (a register load per step carries 64 useful bytes of 1 KiB)
+        // loads (a register load per step carries 64 useful bytes of 1 KiB).
+        // 5 to 16: 32 rows of A per workgroup when that still leaves 192 or
+        // more workgroups (each B fragment then serves two A tiles)
         const int mt = (RB + 15) / 16;
-        if (RB <= 4) SP24_SKINNY(1, true, "sp24_skinny_x4");
-        else if (mt <= 1) SP24_SKINNY(1, false, "sp24_skinny_m16");
-        else if (mt == 2) SP24_SKINNY(2, false, "sp24_skinny_m32");
-        else SP24_SKINNY(4, false, "sp24_skinny_m64");
+        if (RB <= 4) SP24_SKINNY(1, true, 1, 1, "sp24_skinny_x4");
+        else if (mt <= 1 && tiles16 / 2 >= 192) {
+            // three or more workgroups per CU: four waves each hold enough in flight
+            if (tiles16 / 2 >= 3 * 256 && waves > 4)
+                waves = 4;
+            SP24_SKINNY(1, false, 2, 1, "sp24_skinny_m16_a32");
+        }
+        else if (mt <= 1) SP24_SKINNY(1, false, 1, 1, "sp24_skinny_m16");
+        else if (mt == 2) SP24_SKINNY(2, false, 1, 1, "sp24_skinny_m32");
+        else SP24_SKINNY(2, false, 1, 2, "sp24_skinny_m64");
 #undef SP24_SKINNY
     } else if ((int64_t)((RA + 255) / 256) * ((RB + 255) / 256) >= 192) {
         return launch_sp24_gemm_big(g, s, kname);

@@ -135,6 +135,26 @@ def test_exact_integer_bitwise(dt, M, N, K):
         assert np.array_equal(to_host(Yd, oracle.F16), oracle.encode(oracle.F16, R))
 
 
+# one case per decode kernel variant: ragged rows of A (not a multiple of the
+# 16- or 32-row tile) and a partial last group of 8 K steps
+SKINNY = [(1, 100, 704, "sp24_skinny_x4"), (4, 6150, 704, "sp24_skinny_x4"),
+          (9, 300, 704, "sp24_skinny_m16"), (16, 6150, 704, "sp24_skinny_m16_a32"),
+          (7, 6166, 1216, "sp24_skinny_m16_a32"), (30, 200, 704, "sp24_skinny_m32"),
+          (64, 190, 704, "sp24_skinny_m64"), (50, 333, 192, "sp24_skinny_m64")]
+
+
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
+@pytest.mark.parametrize("M,N,K,kernel", SKINNY)
+def test_skinny_variants_exact(dt, M, N, K, kernel):
+    """Every decode kernel variant on exact-integer inputs: bitwise equal to the oracle."""
+    K = K if dt != oracle.E4M3 else 2 * K
+    ttype = {oracle.BF16: torch.bfloat16, oracle.F16: torch.float16, oracle.E4M3: torch.float8_e4m3fn}[dt]
+    assert sp.gemm_kernel(True, sp.SPARSE_W, ttype, torch.float32, M, N, K) == kernel
+    say("skinny", kernel, dt, M, N, K)
+    Y, R, _ = _sparse_w(dt, oracle.F32, M, N, K, seed=M * 7 + N, integer=True)
+    assert np.array_equal(Y, R)
+
+
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.E4M3])
 @pytest.mark.parametrize("M,N,K", [(3, 40, 96), (16, 17, 200), (100, 70, 112), (130, 129, 1040)])
 def test_dense_accepts_k_the_sparse_path_rejects(dt, M, N, K):
