@@ -3,9 +3,9 @@
 // between kernels of the same construction ("Production 2:4 Structured
 // Sparsity for LLMs", section "Sparse Tactic Audit").
 //
-//   - tile 256 (W rows) x 256 (X rows); 4 waves in a 2 x 2 grid, each owning
-//     128 x 128 = 4 x 4 fragments of v_mfma_f32_32x32x16 (16-bit) or
-//     v_mfma_scale_f32_32x32x64_f8f6f4 (fp8, unit scales);
+//   - tile 256 (W rows) x 256 (X rows); 8 waves in a 4 x 2 grid (two per
+//     SIMD), each owning 64 x 128 = 2 x 4 fragments of v_mfma_f32_32x32x16
+//     (16-bit) or v_mfma_scale_f32_32x32x64_f8f6f4 (fp8, unit scales);
 //   - one stage = one 128-byte slice of every row of both operands (64 K for
 //     16-bit, 128 K for fp8): 64 KB; two stages in LDS, filled by direct
 //     global->LDS loads while the other is consumed;
@@ -20,7 +20,10 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBA = 256, kBB = 256, kThreads = 256;
+constexpr int kBA = 256, kBB = 256;
+constexpr int kWA = 4, kWB = 2, kWaves = kWA * kWB, kThreads = 64 * kWaves;
+constexpr int kFA = kBA / 32 / kWA, kFB = kBB / 32 / kWB;   // 32x32 fragments per wave: 2 x 4
+constexpr int kLoads = kBA * 128 / 1024 / kWaves;            // 1 KiB loads per operand and wave: 4
 constexpr int kStage = 256 * 128;   // bytes per operand per stage
 
 template <int N>
@@ -62,14 +65,14 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
           const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K, int tiles_a,
           int tiles_b) {
     using Op = Dense32<DT>;
-    constexpr int LOADS = 2 * kStage / 1024 / 4;   // per wave per stage: 8 (W) + 8 (X)
+    constexpr int LOADS = 2 * kLoads;               // per wave per stage
     __shared__ __attribute__((aligned(1024))) uint8_t a0s[kStage], a1s[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t b0s[kStage], b1s[kStage];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, kg = lane >> 5;
-    const int wa = wave >> 1, wb = wave & 1;
+    const int wa = wave / kWB, wb = wave % kWB;
 
     // ---- tile order: XCD-aware, grouped 4 W tiles x all X tiles
     const int nwg = gridDim.x;
@@ -87,12 +90,12 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
     const Buf bufW(W, (uint32_t)N * row_bytes);           // rows past N / M read as zeros
     const Buf bufX(X, (uint32_t)M * row_bytes);
 
-    // ---- this wave's loads: 8 x 1 KiB of W rows and 8 of X rows per stage
-    uint32_t ga[8], gb[8];
-    int gc[8];   // byte column of the chunk each lane fetches (for the partial last step)
+    // ---- this wave's loads: kLoads x 1 KiB of W rows and as many of X rows per stage
+    uint32_t ga[kLoads], gb[kLoads];
+    int gc[kLoads];   // byte column of the chunk each lane fetches (for the partial last step)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int row = 8 * (8 * wave + j) + (lane >> 3);
+    for (int j = 0; j < kLoads; ++j) {
+        const int row = 8 * (kLoads * wave + j) + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         gc[j] = 16 * c;
         ga[j] = (uint32_t)(a0 + row) * row_bytes + 16 * c;
@@ -105,47 +108,47 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
         const bool live = sl < steps;
         const uint32_t so = (uint32_t)s * 128;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kLoads; ++j) {
             const bool in = live && so + gc[j] < row_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufW.r, (lds_void*)(as + 1024 * (8 * wave + j)), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufW.r, (lds_void*)(as + 1024 * (kLoads * wave + j)), 16,
                                                      (int)(in ? ga[j] : kOOB), (int)(in ? so : 0u), 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kLoads; ++j) {
             const bool in = live && so + gc[j] < row_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufX.r, (lds_void*)(bs + 1024 * (8 * wave + j)), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufX.r, (lds_void*)(bs + 1024 * (kLoads * wave + j)), 16,
                                                      (int)(in ? gb[j] : kOOB), (int)(in ? so : 0u), 0, 0);
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[kFA][kFB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kFA; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kFB; ++j)
             acc[i][j] = (f32x16){};
 
     const int swz = (r >> 1) & 7;
     auto compute = [&](const uint8_t* as, const uint8_t* bs) {
 #pragma unroll
         for (int q = 0; q < Op::SUB; ++q) {
-            uint4 fa[4][Op::CHUNKS], fb[4][Op::CHUNKS];
+            uint4 fa[kFA][Op::CHUNKS], fb[kFB][Op::CHUNKS];
 #pragma unroll
             for (int h = 0; h < Op::CHUNKS; ++h) {
                 // chunk of K this lane supplies: 16-bit 2q + kg; fp8 4q + 2kg + h
                 const int c = Op::CHUNKS == 1 ? 2 * q + kg : 4 * q + 2 * kg + h;
                 const int off = 16 * (c ^ swz);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    fa[i][h] = *reinterpret_cast<const uint4*>(as + (wa * 128 + i * 32 + r) * 128 + off);
+                for (int i = 0; i < kFA; ++i)
+                    fa[i][h] = *reinterpret_cast<const uint4*>(as + (wa * 32 * kFA + i * 32 + r) * 128 + off);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    fb[j][h] = *reinterpret_cast<const uint4*>(bs + (wb * 128 + j * 32 + r) * 128 + off);
+                for (int j = 0; j < kFB; ++j)
+                    fb[j][h] = *reinterpret_cast<const uint4*>(bs + (wb * 32 * kFB + j * 32 + r) * 128 + off);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kFA; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < kFB; ++j)
                     acc[i][j] = Op::mma(fa[i], fb[j], acc[i][j]);
         }
     };
@@ -168,16 +171,16 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
 
     // ---- epilogue: D[8*(v/4) + 4*kg + v%4][r] of fragment (i, j); a = W row (n), b = X row (m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kFA; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = b0 + wb * 128 + j * 32 + r;
+        for (int j = 0; j < kFB; ++j) {
+            const int m = b0 + wb * 32 * kFB + j * 32 + r;
             if (m >= M)
                 continue;
             const float fsx = sx ? sx[m] : 1.f;
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                const int n = a0 + wa * 128 + i * 32 + 8 * h + 4 * kg;
+                const int n = a0 + wa * 32 * kFA + i * 32 + 8 * h + 4 * kg;
                 if (n >= N)
                     continue;
                 f32x4 v;

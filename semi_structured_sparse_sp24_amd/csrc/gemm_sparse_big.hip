@@ -6,9 +6,13 @@
 // Y[a * sya + b * syb] (the paper's section 2, "Sparse tensor cores").
 //
 // Design (one workgroup per CU):
-//   - tile 256 (A rows) x 256 (B rows); 4 waves in a 2 x 2 grid, each owning
-//     128 x 128 = 8 x 8 fragments of v_smfmac_f32_16x16x64 (16-bit) or
-//     v_smfmac_f32_16x16x128 (fp8), accumulated in 256 registers per lane;
+//   - tile 256 (A rows) x 256 (B rows); 8 waves in a 4 x 2 grid (two per
+//     SIMD), each owning 64 x 128 = 4 x 8 fragments of v_smfmac_f32_16x16x64
+//     (16-bit) or v_smfmac_f32_16x16x128 (fp8), accumulated in 128 registers
+//     per lane.  (One wave per SIMD with 128 x 128 each needs 256 accumulator
+//     registers plus operands, and the compiler then shuffles accumulators
+//     between register files inside the loop; two waves per SIMD also hide
+//     each other's LDS latency.)
 //   - K advances one instruction step per stage: A 256 rows x 64 B, metadata
 //     256 rows x 8 (or 16) B, B 256 rows x 128 B = 50 KB; three stages live
 //     in LDS (150 KB of the 160 KB);
@@ -29,7 +33,9 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBA = 256, kBB = 256, kThreads = 256;
+constexpr int kBA = 256, kBB = 256;
+constexpr int kWA = 4, kWB = 2, kWaves = kWA * kWB, kThreads = 64 * kWaves;
+constexpr int kFA = kBA / 16 / kWA, kFB = kBB / 16 / kWB;   // 16x16 fragments per wave: 4 x 8
 constexpr int kAStage = kBA * 64;     // bytes of compressed A per stage
 constexpr int kBStage = kBB * 128;    // bytes of dense B per stage
 
@@ -61,9 +67,9 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
     using Op = SparseOp<DT>;
     constexpr int MWS = L::META_WORDS;                  // metadata words per row per step: 2 or 4
     constexpr int kMStage = kBA * MWS * 4;
-    constexpr int A_LOADS = kAStage / 1024 / 4;         // per wave: 4
-    constexpr int B_LOADS = kBStage / 1024 / 4;         // per wave: 8
-    constexpr int M_LOADS = kMStage / 256 / 4;          // per wave (dword loads): 2 or 4
+    constexpr int A_LOADS = kAStage / 1024 / kWaves;    // per wave: 2
+    constexpr int B_LOADS = kBStage / 1024 / kWaves;    // per wave: 4
+    constexpr int M_LOADS = kMStage / 256 / kWaves;     // per wave (dword loads): 1 or 2
     constexpr int LOADS = A_LOADS + B_LOADS + M_LOADS;  // per wave per stage
 
     __shared__ __attribute__((aligned(1024))) uint8_t a0s[kAStage], a1s[kAStage], a2s[kAStage];
@@ -73,7 +79,7 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int r = lane & 15, kg = lane >> 4;
-    const int wa = wave >> 1, wb = wave & 1;
+    const int wa = wave / kWB, wb = wave % kWB;
 
     // ---- tile order: XCD-aware, grouped 4 A tiles x all B tiles
     const int nwg = gridDim.x;
@@ -98,7 +104,7 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
         const int row = 16 * (A_LOADS * wave + j) + (lane >> 2);
-        const int c = (lane & 3) ^ ((row >> 2) & 3);             // chunk stored in slot lane & 3
+        const int c = (lane & 3) ^ ((row >> 1) & 3);             // chunk stored in slot lane & 3
         ga[j] = (uint32_t)(a0 + row) * a_row_bytes + 16 * c;
     }
 #pragma unroll
@@ -137,33 +143,33 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
     };
 
     // ---- fragment read offsets (bytes within a stage)
-    const int a_frag = (wa * 128 + r) * 64 + 16 * (kg ^ ((r >> 2) & 3));
-    const int m_frag = ((wa * 128 + r) * MWS + L::meta_word(kg)) * 4;
+    const int a_frag = (wa * 16 * kFA + r) * 64 + 16 * (kg ^ ((r >> 1) & 3));
+    const int m_frag = ((wa * 16 * kFA + r) * MWS + L::meta_word(kg)) * 4;
     const int msh = L::meta_shift(kg);
-    const int b_frag0 = (wb * 128 + r) * 128 + 16 * (kg ^ ((r >> 1) & 7));
-    const int b_frag1 = (wb * 128 + r) * 128 + 16 * ((4 + kg) ^ ((r >> 1) & 7));
+    const int b_frag0 = (wb * 16 * kFB + r) * 128 + 16 * (kg ^ ((r >> 1) & 7));
+    const int b_frag1 = (wb * 16 * kFB + r) * 128 + 16 * ((4 + kg) ^ ((r >> 1) & 7));
 
-    f32x4 acc[8][8];
+    f32x4 acc[kFA][kFB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kFA; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < kFB; ++j)
             acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const uint8_t* as, const uint8_t* bs, const uint8_t* ms) {
-        uint4 fa[8];
-        uint32_t fi[8];
+        uint4 fa[kFA];
+        uint32_t fi[kFA];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kFA; ++i) {
             fa[i] = *reinterpret_cast<const uint4*>(as + a_frag + i * 16 * 64);
             fi[i] = *reinterpret_cast<const uint32_t*>(ms + m_frag + i * 16 * MWS * 4) >> msh;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kFB; ++j) {
             const uint4 fb0 = *reinterpret_cast<const uint4*>(bs + b_frag0 + j * 16 * 128);
             const uint4 fb1 = *reinterpret_cast<const uint4*>(bs + b_frag1 + j * 16 * 128);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < kFA; ++i)
                 acc[i][j] = Op::mma(fa[i], fb0, fb1, fi[i], acc[i][j]);
         }
     };
@@ -196,11 +202,11 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
 
     // ---- epilogue: fragment (i, j), lane -> D[a][b], a = .. + 4*kg + q, b = .. + r
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kFA; ++i) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int ar = a0 + wa * 128 + i * 16 + 4 * kg;
-            const int br = b0 + wb * 128 + j * 16 + r;
+        for (int j = 0; j < kFB; ++j) {
+            const int ar = a0 + wa * 16 * kFA + i * 16 + 4 * kg;
+            const int br = b0 + wb * 16 * kFB + j * 16 + r;
             if (br >= RB || ar >= RA)
                 continue;
             f32x4 v = acc[i][j];
