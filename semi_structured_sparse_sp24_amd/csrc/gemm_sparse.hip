@@ -16,8 +16,7 @@
 //           of a group at once (A into registers, metadata and up to 4 B rows
 //           into LDS by direct global->LDS loads), and reduce their partial
 //           tiles through LDS in a fixed order (deterministic, no atomics).
-// Larger B goes to the tiled kernels (gemm_sparse_tiled.hip for mid-size
-// outputs, gemm_sparse_big.hip once 256 x 256 tiles fill the chip).
+// Larger B goes to the LDS-staged tile kernels of gemm_sparse_big.hip.
 #include "mfma_ops.h"
 
 namespace sp24 {
@@ -229,7 +228,10 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
     const uint8_t* av = (const uint8_t*)g.a_vals;
     const uint8_t* b = (const uint8_t*)g.b;
     const int tiles16 = (RA + 15) / 16;
-    if (RB <= 64) {
+    // 17 to 64 dense rows: the tile kernels once 128-row tiles of A give
+    // every CU a workgroup; until then the decode kernel, whose workgroups
+    // split K and so stay many on narrow outputs
+    if (RB <= 16 || (RB <= 64 && (RA + 127) / 128 < 128)) {
         const int steps = (int)(g.K / SparseOp<DT>::KSTEP);
         const int groups = (steps + kGroup - 1) / kGroup;
         // as many waves as there are load groups to split, up to 8 (measured
@@ -261,10 +263,10 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
         else if (mt == 2) SP24_SKINNY(2, false, 1, 1, "sp24_skinny_m32");
         else SP24_SKINNY(2, false, 1, 2, "sp24_skinny_m64");
 #undef SP24_SKINNY
-    } else if ((int64_t)((RA + 255) / 256) * ((RB + 255) / 256) >= 192) {
-        return launch_sp24_gemm_big(g, s, kname);
     } else {
-        return launch_sp24_gemm_tiled(g, s, kname);
+        // the LDS-staged tile kernels, which read each B fragment once per
+        // 128 or 256 rows of A
+        return launch_sp24_gemm_big(g, s, kname);
     }
     return g.dry ? hipSuccess : hipGetLastError();
 }

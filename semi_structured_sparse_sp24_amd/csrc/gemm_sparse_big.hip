@@ -1,11 +1,12 @@
-// gemm_sparse_big.hip -- 2:4 sparse x dense GEMM for large M (prefill,
-// dynamic operands) on gfx950 SMFMAC.
+// gemm_sparse_big.hip -- 2:4 sparse x dense GEMM for large outputs (prefill,
+// dynamic operands, and the 17-64 row decode cases) on gfx950 SMFMAC.
 //
 // Same contract as the kernels in gemm_sparse.hip: D[a][b] = sum_k A[a][k] *
 // B[b][k] with A compressed (values + metadata) and B dense, stored to
 // Y[a * sya + b * syb] (the paper's section 2, "Sparse tensor cores").
 //
-// Design (one workgroup per CU):
+// Design (shown for the 256 x 256 tile; smaller tiles for outputs that would
+// not fill the chip follow the same plan with fewer rows):
 //   - tile 256 (A rows) x 256 (B rows); 8 waves in a 4 x 2 grid (two per
 //     SIMD), each owning 64 x 128 = 4 x 8 fragments of v_smfmac_f32_16x16x64
 //     (16-bit) or v_smfmac_f32_16x16x128 (fp8), accumulated in 128 registers
@@ -13,9 +14,10 @@
 //     registers plus operands, and the compiler then shuffles accumulators
 //     between register files inside the loop; two waves per SIMD also hide
 //     each other's LDS latency.)
-//   - K advances one instruction step per stage: A 256 rows x 64 B, metadata
-//     256 rows x 8 (or 16) B, B 256 rows x 128 B = 50 KB; three stages live
-//     in LDS (150 KB of the 160 KB);
+//   - K advances one instruction step per stage: A 256 rows x 64 B and B 256
+//     rows x 128 B; metadata comes in blocks of 16 B per row (two 16-bit
+//     steps, or one fp8 step); three stages and three metadata blocks live in
+//     LDS (156 KB of the 160 KB);
 //   - the stages are filled by direct global->LDS loads (buffer_load_dwordx4
 //     ... lds): no registers, no LDS write instructions; two steps are in
 //     flight while the third is consumed, with one barrier per step;
@@ -33,11 +35,21 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBA = 256, kBB = 256;
-constexpr int kWA = 4, kWB = 2, kWaves = kWA * kWB, kThreads = 64 * kWaves;
-constexpr int kFA = kBA / 16 / kWA, kFB = kBB / 16 / kWB;   // 16x16 fragments per wave: 4 x 8
-constexpr int kAStage = kBA * 64;     // bytes of compressed A per stage
-constexpr int kBStage = kBB * 128;    // bytes of dense B per stage
+// Tile shapes: BA rows of A x BB rows of B, WA x WB waves, OCC workgroups per CU.
+template <int BA_, int BB_, int WA_, int WB_, int OCC_>
+struct Tile {
+    static constexpr int BA = BA_, BB = BB_, WA = WA_, WB = WB_, OCC = OCC_;
+    static constexpr int WAVES = WA * WB, THREADS = 64 * WAVES;
+    static constexpr int FA = BA / 16 / WA, FB = BB / 16 / WB;   // 16x16 fragments per wave
+    static constexpr int A_STAGE = BA * 64;    // bytes of compressed A per stage
+    static constexpr int B_STAGE = BB * 128;   // bytes of dense B per stage
+    static constexpr int M_BLOCK = BA * 16;    // bytes of one metadata block
+};
+using T256x256 = Tile<256, 256, 4, 2, 1>;
+using T256x128 = Tile<256, 128, 4, 2, 1>;
+using T128x128 = Tile<128, 128, 2, 4, 2>;
+using T256x64 = Tile<256, 64, 4, 2, 1>;
+using T128x64 = Tile<128, 64, 4, 2, 2>;
 
 __device__ __forceinline__ void dma16(const Buf& b, void* lds_base, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_void*)lds_base, 16, (int)voff, (int)soff, 0, 0);
@@ -58,23 +70,31 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-template <sp24_dtype DT, sp24_dtype OUT>
-__global__ void __launch_bounds__(kThreads, 1)
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
+__global__ void __launch_bounds__(TL::THREADS, TL::OCC)
 sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const uint8_t* __restrict__ B,
          const float* __restrict__ sa, const float* __restrict__ sb, void* __restrict__ Y, int RA, int RB,
          int64_t K, int64_t sya, int64_t syb, int tiles_a, int tiles_b) {
     using L = StepLayout<DT>;
     using Op = SparseOp<DT>;
     constexpr int MWS = L::META_WORDS;                  // metadata words per row per step: 2 or 4
-    constexpr int kMStage = kBA * MWS * 4;
-    constexpr int A_LOADS = kAStage / 1024 / kWaves;    // per wave: 2
-    constexpr int B_LOADS = kBStage / 1024 / kWaves;    // per wave: 4
-    constexpr int M_LOADS = kMStage / 256 / kWaves;     // per wave (dword loads): 1 or 2
-    constexpr int LOADS = A_LOADS + B_LOADS + M_LOADS;  // per wave per stage
+    // metadata goes in blocks of 16 bytes per row: T steps (2 for 16-bit, 1
+    // for fp8), one 16-byte load per row -- a request per row per block where
+    // per-step 4-byte loads cost a request per row per step
+    constexpr int T = 4 / MWS;
+    constexpr int kBA = TL::BA, kBB = TL::BB, kWB = TL::WB, kWaves = TL::WAVES, kFA = TL::FA, kFB = TL::FB;
+    constexpr int kAStage = TL::A_STAGE, kBStage = TL::B_STAGE, kMBlock = TL::M_BLOCK;
+    constexpr int M_WAVES = kMBlock / 1024;             // waves that issue a block's 1 KiB loads
+    constexpr int A_LOADS = kAStage / 1024 / kWaves;    // per wave
+    constexpr int B_LOADS = kBStage / 1024 / kWaves;    // per wave
+    static_assert(A_LOADS * kWaves * 1024 == kAStage && B_LOADS * kWaves * 1024 == kBStage, "whole loads per wave");
+    static_assert(M_WAVES * 1024 == kMBlock && M_WAVES <= kWaves, "metadata block");
+    constexpr int AB = A_LOADS + B_LOADS;
+    constexpr int U = 3 * T;                            // loop unroll: a whole number of stages and blocks
 
     __shared__ __attribute__((aligned(1024))) uint8_t a0s[kAStage], a1s[kAStage], a2s[kAStage];
     __shared__ __attribute__((aligned(1024))) uint8_t b0s[kBStage], b1s[kBStage], b2s[kBStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t m0s[kMStage], m1s[kMStage], m2s[kMStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t m0s[kMBlock], m1s[kMBlock], m2s[kMBlock];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -100,7 +120,7 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
     const Buf bufB(B, (uint32_t)RB * b_row_bytes);
 
     // ---- per-lane global offsets of this wave's loads (step 0), and LDS slots
-    uint32_t ga[A_LOADS], gb[B_LOADS], gm[M_LOADS];
+    uint32_t ga[A_LOADS], gb[B_LOADS];
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
         const int row = 16 * (A_LOADS * wave + j) + (lane >> 2);
@@ -113,16 +133,15 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         gb[j] = (uint32_t)(b0 + row) * b_row_bytes + 16 * c;
     }
-#pragma unroll
-    for (int j = 0; j < M_LOADS; ++j) {
-        const int w = 64 * (M_LOADS * wave + j) + lane;           // metadata word of the stage
-        gm[j] = (uint32_t)(a0 + w / MWS) * m_row_bytes + 4 * (w % MWS);
-    }
+    // metadata: wave w < M_WAVES loads rows [64 w, 64 w + 64), 16 bytes each
+    const uint32_t gm = (uint32_t)(a0 + 64 * min(wave, M_WAVES - 1) + lane) * m_row_bytes;
 
     // K loop start rotated per group of tile-sharing workgroups: members of a
     // group (resident together on one XCD) walk K in step and share operand
-    // slices through L2, while different groups spread over memory channels
-    const int rot = (int)(((unsigned)group * 13u) % (unsigned)steps);
+    // slices through L2, while different groups spread over memory channels.
+    // The rotation keeps metadata blocks aligned (a multiple of T), and is
+    // dropped when the step count is not a multiple of T.
+    const int rot = steps % T ? 0 : (int)(((unsigned)group * 13u) % (unsigned)(steps / T)) * T;
     auto issue = [&](uint8_t* as, uint8_t* bs, uint8_t* ms, int sl) {
         // step sl of the rotated K loop; steps past the end load nothing useful
         int s = sl + rot;
@@ -130,21 +149,29 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
         const bool live = sl < steps;
         const uint32_t sA = live ? (uint32_t)s * L::A_STEP_BYTES : kOOB;
         const uint32_t sB = live ? (uint32_t)s * L::B_STEP_BYTES : kOOB;
-        const uint32_t sM = live ? (uint32_t)s * (4 * MWS) : kOOB;
 #pragma unroll
         for (int j = 0; j < A_LOADS; ++j)
             dma16(bufA, as + 1024 * (A_LOADS * wave + j), ga[j], sA);
 #pragma unroll
         for (int j = 0; j < B_LOADS; ++j)
             dma16(bufB, bs + 1024 * (B_LOADS * wave + j), gb[j], sB);
-#pragma unroll
-        for (int j = 0; j < M_LOADS; ++j)
-            dma4(bufM, ms + 256 * (M_LOADS * wave + j), gm[j], sM);
+        // the block of steps s .. s + T - 1 (with T = 2 and an odd step count,
+        // the last block's second half is past the row: read, never used)
+        if (ms != nullptr && wave < M_WAVES)
+            dma16(bufM, ms + 1024 * wave, gm, live ? (uint32_t)s * (4 * MWS) : kOOB);
+    };
+    // before computing step x: this wave's loads of step x have landed when
+    // only those of step x + 1 (issued one step later) may be outstanding
+    auto wait_step = [&](bool next_has_meta) {
+        if (next_has_meta && wave < M_WAVES)
+            wait_vmcnt_lgkm0<AB + 1>();
+        else
+            wait_vmcnt_lgkm0<AB>();
     };
 
-    // ---- fragment read offsets (bytes within a stage)
+    // ---- fragment read offsets (bytes within a stage / a metadata block)
     const int a_frag = (wa * 16 * kFA + r) * 64 + 16 * (kg ^ ((r >> 1) & 3));
-    const int m_frag = ((wa * 16 * kFA + r) * MWS + L::meta_word(kg)) * 4;
+    const int m_frag = (wa * 16 * kFA + r) * 16 + 4 * L::meta_word(kg);
     const int msh = L::meta_shift(kg);
     const int b_frag0 = (wb * 16 * kFB + r) * 128 + 16 * (kg ^ ((r >> 1) & 7));
     const int b_frag1 = (wb * 16 * kFB + r) * 128 + 16 * ((4 + kg) ^ ((r >> 1) & 7));
@@ -156,13 +183,14 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
         for (int j = 0; j < kFB; ++j)
             acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const uint8_t* as, const uint8_t* bs, const uint8_t* ms) {
+    // u: the step's position within its metadata block
+    auto compute = [&](const uint8_t* as, const uint8_t* bs, const uint8_t* ms, int u) {
         uint4 fa[kFA];
         uint32_t fi[kFA];
 #pragma unroll
         for (int i = 0; i < kFA; ++i) {
             fa[i] = *reinterpret_cast<const uint4*>(as + a_frag + i * 16 * 64);
-            fi[i] = *reinterpret_cast<const uint32_t*>(ms + m_frag + i * 16 * MWS * 4) >> msh;
+            fi[i] = *reinterpret_cast<const uint32_t*>(ms + m_frag + 4 * MWS * u + i * 16 * 16) >> msh;
         }
 #pragma unroll
         for (int j = 0; j < kFB; ++j) {
@@ -174,29 +202,29 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
         }
     };
 
-    // ---- pipeline: stages 0 and 1 in flight, then one step per stage
-    // block.  Before each block a wave waits for its own loads of the stage
-    // it is about to read (the next stage's may stay in flight) and for its
-    // LDS reads of the previous stage, then a barrier makes every wave's
-    // loads visible and frees the stage the new loads overwrite.  The step
-    // count is padded to a multiple of 3 (padded steps read zeros) so the loop
-    // body has no exits: that keeps the accumulators in registers.
-    issue(a0s, b0s, m0s, 0);
-    issue(a1s, b1s, m1s, 1);
-    const int steps3 = (steps + 2) / 3 * 3;
-    for (int s = 0; s < steps3; s += 3) {
-        wait_vmcnt_lgkm0<LOADS>();
-        __builtin_amdgcn_s_barrier();
-        issue(a2s, b2s, m2s, s + 2);
-        compute(a0s, b0s, m0s);
-        wait_vmcnt_lgkm0<LOADS>();
-        __builtin_amdgcn_s_barrier();
-        issue(a0s, b0s, m0s, s + 3);
-        compute(a1s, b1s, m1s);
-        wait_vmcnt_lgkm0<LOADS>();
-        __builtin_amdgcn_s_barrier();
-        issue(a1s, b1s, m1s, s + 4);
-        compute(a2s, b2s, m2s);
+    // ---- pipeline: steps x and x + 1 in flight while x - 1 is consumed; one
+    // barrier per step.  Before each step a wave waits for its own loads of
+    // that step and for its LDS reads of the previous one; the barrier makes
+    // every wave's loads visible and frees the stage the new loads overwrite.
+    // Stage of step x: x % 3; metadata block of step x: (x / T) % 3, loaded
+    // with the stage of its first step.  The loop runs U = 3 T steps per
+    // iteration (padded steps read zeros) so that both indices are static and
+    // the body has no exits, which keeps the accumulators in registers.
+    uint8_t* const as_[3] = {a0s, a1s, a2s};
+    uint8_t* const bs_[3] = {b0s, b1s, b2s};
+    uint8_t* const ms_[3] = {m0s, m1s, m2s};
+    issue(as_[0], bs_[0], ms_[0], 0);
+    issue(as_[1], bs_[1], 1 % T ? nullptr : ms_[1 / T], 1);
+    const int stepsU = (steps + U - 1) / U * U;
+    for (int s = 0; s < stepsU; s += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            wait_step((u + 1) % T == 0);
+            __builtin_amdgcn_s_barrier();
+            const int x2 = u + 2;   // issued now: position within the unrolled block
+            issue(as_[x2 % 3], bs_[x2 % 3], x2 % T ? nullptr : ms_[(x2 / T) % 3], s + x2);
+            compute(as_[u % 3], bs_[u % 3], ms_[(u / T) % 3], u % T);
+        }
     }
     wait_vmcnt<0>();   // drain the (useless) loads of steps past the end
 
@@ -227,20 +255,42 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
     }
 }
 
-template <sp24_dtype DT, sp24_dtype OUT>
-hipError_t launch_big(const GemmArgs& g, hipStream_t s, const char** kname) {
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
+hipError_t launch_tile(const GemmArgs& g, hipStream_t s, const char** kname, const char* name) {
     const int RA = (int)(g.a_is_w ? g.N : g.M);
     const int RB = (int)(g.a_is_w ? g.M : g.N);
     const int64_t sya = g.a_is_w ? 1 : g.N, syb = g.a_is_w ? g.N : 1;
-    const int tiles_a = (RA + kBA - 1) / kBA, tiles_b = (RB + kBB - 1) / kBB;
+    const int tiles_a = (RA + TL::BA - 1) / TL::BA, tiles_b = (RB + TL::BB - 1) / TL::BB;
     if (kname)
-        *kname = "sp24_big_256x256";
+        *kname = name;
     if (g.dry)
         return hipSuccess;
-    hipLaunchKernelGGL((sp24_big<DT, OUT>), dim3(tiles_a * tiles_b), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((sp24_big<DT, OUT, TL>), dim3(tiles_a * tiles_b), dim3(TL::THREADS), 0, s,
                        (const uint8_t*)g.a_vals, g.a_meta, (const uint8_t*)g.b, g.scale_a, g.scale_b, g.Y, RA,
                        RB, g.K, sya, syb, tiles_a, tiles_b);
     return hipGetLastError();
+}
+
+template <class TL>
+int64_t tiles_of(const GemmArgs& g) {
+    const int64_t RA = g.a_is_w ? g.N : g.M, RB = g.a_is_w ? g.M : g.N;
+    return ((RA + TL::BA - 1) / TL::BA) * ((RB + TL::BB - 1) / TL::BB) * TL::OCC;
+}
+
+// The largest tile that keeps most CUs busy (measured: 256 x 256 from 192
+// tiles on); failing that, the smallest.  The smaller tiles run two
+// workgroups per CU.
+template <sp24_dtype DT, sp24_dtype OUT>
+hipError_t launch_big(const GemmArgs& g, hipStream_t s, const char** kname) {
+    const int64_t RB = g.a_is_w ? g.M : g.N;
+    constexpr int64_t kFill = 192;
+    if (RB > 64) {
+        if (tiles_of<T256x256>(g) >= kFill) return launch_tile<DT, OUT, T256x256>(g, s, kname, "sp24_big_256x256");
+        if (tiles_of<T256x128>(g) >= kFill) return launch_tile<DT, OUT, T256x128>(g, s, kname, "sp24_big_256x128");
+        return launch_tile<DT, OUT, T128x128>(g, s, kname, "sp24_big_128x128");
+    }
+    if (tiles_of<T256x64>(g) >= kFill) return launch_tile<DT, OUT, T256x64>(g, s, kname, "sp24_big_256x64");
+    return launch_tile<DT, OUT, T128x64>(g, s, kname, "sp24_big_128x64");
 }
 
 }  // namespace

@@ -49,9 +49,8 @@ struct GemmArgs {
 // Sparse GEMM; writes the name of the kernel it launched into kname (if
 // non-null).  With g.dry set, launches nothing and returns hipSuccess.
 hipError_t launch_sp24_gemm(const GemmArgs& g, hipStream_t s, const char** kname);
-// The 128 x 128-tile sparse kernel for mid-size outputs (called by launch_sp24_gemm).
-hipError_t launch_sp24_gemm_tiled(const GemmArgs& g, hipStream_t s, const char** kname);
-// The 256 x 256-tile sparse kernel for large M (called by launch_sp24_gemm).
+// The LDS-staged tile kernels (256 x 256 down to 128 x 64 tiles) for outputs
+// with more than 16 dense rows (called by launch_sp24_gemm).
 hipError_t launch_sp24_gemm_big(const GemmArgs& g, hipStream_t s, const char** kname);
 
 struct DenseArgs {

@@ -106,10 +106,12 @@ def test_gemm_kernel_names_follow_the_dispatch():
     assert k(True, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "sp24_skinny_m16"
     assert k(True, sp.SPARSE_W, bf, bf, 64, 4096, 4096) == "sp24_skinny_m64"
     assert k(False, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "dense_skinny_m1"
-    # large outputs take the 256 x 256 tiles once they fill the chip (192 tiles)
+    # beyond 16 rows: the largest LDS-staged tile that still fills the chip
     assert k(True, sp.SPARSE_W, bf, bf, 8192, 4096, 4096) == "sp24_big_256x256"
+    assert k(True, sp.SPARSE_W, bf, bf, 2048, 4096, 4096) == "sp24_big_256x128"
+    assert k(True, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "sp24_big_128x128"
+    assert k(True, sp.SPARSE_W, bf, bf, 64, 28672, 4096) == "sp24_big_128x64"
     assert k(False, sp.SPARSE_W, bf, bf, 8192, 4096, 4096) == "dense_big_256x256"
-    assert k(True, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "sp24_tiled_128x128"
     # rejected shapes and degenerate ones
     assert k(True, sp.SPARSE_W, bf, bf, 4, 4096, 96) is None
     assert k(False, sp.SPARSE_W, bf, bf, 4, 4096, 100) is None

@@ -140,13 +140,15 @@ def test_exact_integer_bitwise(dt, M, N, K):
 SKINNY = [(1, 100, 704, "sp24_skinny_x4"), (4, 6150, 704, "sp24_skinny_x4"),
           (9, 300, 704, "sp24_skinny_m16"), (16, 6150, 704, "sp24_skinny_m16_a32"),
           (7, 6166, 1216, "sp24_skinny_m16_a32"), (30, 200, 704, "sp24_skinny_m32"),
-          (64, 190, 704, "sp24_skinny_m64"), (50, 333, 192, "sp24_skinny_m64")]
+          (64, 190, 704, "sp24_skinny_m64"), (50, 333, 192, "sp24_skinny_m64"),
+          (40, 17000, 704, "sp24_big_128x64"), (17, 61500, 192, "sp24_big_256x64")]
 
 
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
 @pytest.mark.parametrize("M,N,K,kernel", SKINNY)
 def test_skinny_variants_exact(dt, M, N, K, kernel):
-    """Every decode kernel variant on exact-integer inputs: bitwise equal to the oracle."""
+    """Every kernel variant of the few-row range on exact-integer inputs:
+    bitwise equal to the oracle."""
     K = K if dt != oracle.E4M3 else 2 * K
     ttype = {oracle.BF16: torch.bfloat16, oracle.F16: torch.float16, oracle.E4M3: torch.float8_e4m3fn}[dt]
     assert sp.gemm_kernel(True, sp.SPARSE_W, ttype, torch.float32, M, N, K) == kernel
@@ -169,17 +171,21 @@ def test_dense_accepts_k_the_sparse_path_rejects(dt, M, N, K):
 
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
 @pytest.mark.parametrize("which", ["sparse_w", "sparse_x", "dense"])
-def test_large_tile_kernels_ragged(dt, which):
-    """Shapes with >= 192 tiles of 256 x 256 run the large-tile kernels; these
-    have ragged last tiles in both dimensions (and, for dense, a partial last
-    K step).  Integer inputs: sampled rows must match the oracle exactly."""
-    M, N = 3000, 4100
-    K = 384 if dt != oracle.E4M3 else 512
+@pytest.mark.parametrize("steps", [6, 7])
+@pytest.mark.parametrize("MN", [(3000, 4100), (3000, 3000), (600, 1000)])
+def test_large_tile_kernels_ragged(dt, which, steps, MN):
+    """The LDS-staged tile kernels (sparse 256x256, 256x128, 128x128; dense
+    256x256 and 128x128) on ragged last tiles in both dimensions (and, for
+    dense, a partial last K step), with an even and an odd count of K steps
+    (the sparse kernels load metadata two 16-bit steps at a time).  Integer
+    inputs: sampled rows must match the oracle exactly."""
+    M, N = MN
+    K = steps * (64 if dt != oracle.E4M3 else 128)
     if which == "dense":
         K += 16                     # not a whole 64-K (128-K) step
     say("large ragged", which, dt, M, N, K)
     xb, _, wb, _ = _operands(dt, M, N, K, 123, integer=True)
-    rows = np.array([0, 1, 255, 256, 1777, 2999])
+    rows = np.array([0, 1, 255, 256, M // 2 + 1, M - 1])
     X, W = to_dev(xb, dt), to_dev(wb, dt)
     if which == "sparse_w":
         wv, wm = oracle.prune_compress(dt, wb)
