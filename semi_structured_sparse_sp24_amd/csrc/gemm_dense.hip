@@ -3,14 +3,14 @@
 // The baseline every sparse tactic is timed against and the target of every
 // fallback ("Production 2:4 Structured Sparsity for LLMs", sections "Sparse
 // Tactic Audit" and "Dense Fallback and Hybrid Sparsity Design").  It has
-// the same two shapes as the sparse kernels so that the comparison is
-// between kernels of the same construction:
-//   skinny  M <= 64: the workgroup owns 16 rows of W and all of X; waves
-//           split K; v_mfma_f32_16x16x32 (16-bit, two per 64-K step) or
-//           v_mfma_scale_f32_16x16x128_f8f6f4 (fp8, unit scales).
-//   tiled   128 x 128 tile, double-buffered LDS, 2 x 2 waves each owning
-//           2 x 2 fragments of v_mfma_f32_32x32x16 (16-bit) or
-//           v_mfma_scale_f32_32x32x64_f8f6f4 (fp8).
+// the same two constructions, and the same split between them, as the sparse
+// kernels so that the comparison is between kernels of the same design:
+//   skinny  few rows of X (<= 16, or <= 64 on a narrow output): the
+//           workgroup owns 16 rows of W and all of X; waves split K;
+//           v_mfma_f32_16x16x32 (16-bit, two per 64-K step) or
+//           v_mfma_scale_f32_16x16x128_f8f6f4 (fp8, unit scales);
+//   tiles   everything else: the LDS-staged tile kernels of
+//           gemm_dense_big.hip.
 // D is computed with A = W (rows N) and B = X (rows M), i.e. the tile of
 // Y^T, and stored transposed.
 #include "mfma_ops.h"
@@ -173,151 +173,14 @@ dense_skinny(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const
     }
 }
 
-// ------------------------------------------------------------------ tiled
-template <sp24_dtype DT, sp24_dtype OUT, int FA, int FB>
-__global__ void __launch_bounds__(256)
-dense_tiled(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
-            const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K, int tiles_n) {
-    using Op = DenseOp32<DT>;
-    constexpr int BA = 2 * FA * 32, BB = 2 * FB * 32;
-    constexpr int STEP_BYTES = Op::KSTEP * Op::ELEM;     // 128
-    constexpr int STRIDE = STEP_BYTES + 16;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BA * STRIDE];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BB * STRIDE];
-
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = lane & 31, kg = lane >> 5;
-    const int wa = wave >> 1, wb = wave & 1;
-    const int ta = blockIdx.x % tiles_n, tb = blockIdx.x / tiles_n;
-    const int a0 = ta * BA, b0 = tb * BB;
-    const int steps = (int)((K + Op::KSTEP - 1) / Op::KSTEP);   // the last step may be partial
-    const int64_t row_bytes = K * Op::ELEM;
-
-    constexpr int A_CHUNKS = BA * 8 / 256, B_CHUNKS = BB * 8 / 256;
-    const int chunk_col = (tid & 7) * 16;   // byte column of this thread's chunks in a step
-    const Buf bufW(W, (uint32_t)N * (uint32_t)row_bytes);   // rows past N / M read as zeros
-    const Buf bufX(X, (uint32_t)M * (uint32_t)row_bytes);
-    uint32_t ga[A_CHUNKS];
-    int la[A_CHUNKS];
-#pragma unroll
-    for (int j = 0; j < A_CHUNKS; ++j) {
-        int c = tid + j * 256, row = c >> 3, col = c & 7;
-        ga[j] = (uint32_t)(a0 + row) * (uint32_t)row_bytes + col * 16;
-        la[j] = row * STRIDE + col * 16;
-    }
-    uint32_t gb[B_CHUNKS];
-    int lb[B_CHUNKS];
-#pragma unroll
-    for (int j = 0; j < B_CHUNKS; ++j) {
-        int c = tid + j * 256, row = c >> 3, col = c & 7;
-        gb[j] = (uint32_t)(b0 + row) * (uint32_t)row_bytes + col * 16;
-        lb[j] = row * STRIDE + col * 16;
-    }
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-    // K loop rotated per workgroup (as in the sparse kernel)
-    const int rot = (int)((blockIdx.x * 13u) % (unsigned)steps);
-    auto gload = [&](int sl) {
-        const int s = sl + rot >= steps ? sl + rot - steps : sl + rot;
-        // a 16-byte chunk past K (a partial last step) reads as zeros
-        const bool in = (int64_t)s * STEP_BYTES + chunk_col < row_bytes;
-        const uint32_t ks = in ? (uint32_t)s * STEP_BYTES : kOOB;
-#pragma unroll
-        for (int j = 0; j < A_CHUNKS; ++j)
-            ra[j] = bufW.ld16(ga[j] + ks);
-#pragma unroll
-        for (int j = 0; j < B_CHUNKS; ++j)
-            rb[j] = bufX.ld16(gb[j] + ks);
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < A_CHUNKS; ++j)
-            *reinterpret_cast<uint4*>(&lds_a[buf][la[j]]) = ra[j];
-#pragma unroll
-        for (int j = 0; j < B_CHUNKS; ++j)
-            *reinterpret_cast<uint4*>(&lds_b[buf][lb[j]]) = rb[j];
-    };
-
-    f32x16 acc[FA][FB];
-#pragma unroll
-    for (int i = 0; i < FA; ++i)
-#pragma unroll
-        for (int j = 0; j < FB; ++j)
-            acc[i][j] = (f32x16){};
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int s = 0; s < steps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < steps)
-            gload(s + 1);
-#pragma unroll
-        for (int q = 0; q < Op::SUB; ++q) {
-            // 16-bit: this lane's 16 B at q*32 + 16*kg; fp8: 32 B at q*64 + 32*kg
-            const int off0 = q * Op::SUB_BYTES + (Op::ELEM == 2 ? 16 * kg : 32 * kg);
-            const int off1 = off0 + 16;
-            uint4 fa0[FA], fa1[FA];
-#pragma unroll
-            for (int i = 0; i < FA; ++i) {
-                const uint8_t* p = &lds_a[buf][(wa * FA * 32 + i * 32 + r) * STRIDE];
-                fa0[i] = *reinterpret_cast<const uint4*>(p + off0);
-                if (Op::ELEM == 1)
-                    fa1[i] = *reinterpret_cast<const uint4*>(p + off1);
-                else
-                    fa1[i] = zero;
-            }
-#pragma unroll
-            for (int j = 0; j < FB; ++j) {
-                const uint8_t* p = &lds_b[buf][(wb * FB * 32 + j * 32 + r) * STRIDE];
-                uint4 fb0 = *reinterpret_cast<const uint4*>(p + off0);
-                uint4 fb1 = Op::ELEM == 1 ? *reinterpret_cast<const uint4*>(p + off1) : zero;
-#pragma unroll
-                for (int i = 0; i < FA; ++i)
-                    acc[i][j] = Op::mma(fa0[i], fa1[i], fb0, fb1, acc[i][j]);
-            }
-        }
-        if (s + 1 < steps)
-            lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // D[8*(q/4) + 4*kg + q%4][r] of fragment (i, j): a = W row, b = X row
-#pragma unroll
-    for (int i = 0; i < FA; ++i) {
-#pragma unroll
-        for (int j = 0; j < FB; ++j) {
-            const int m = b0 + wb * FB * 32 + j * 32 + r;
-            if (m >= M)
-                continue;
-            const float fsx = sx ? sx[m] : 1.f;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const int n = a0 + wa * FA * 32 + i * 32 + 8 * h + 4 * kg;
-                f32x4 v;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    v[q] = acc[i][j][4 * h + q] * fsx * (sw && n + q < N ? sw[n + q] : 1.f);
-                const int64_t off = (int64_t)m * N + n;
-                if (n + 3 < N && (off & 3) == 0) {
-                    store_out4<OUT>(Y, off, v);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (n + q < N)
-                            store_out<OUT>(Y, off + q, v[q]);
-                }
-            }
-        }
-    }
-}
-
 template <sp24_dtype DT, sp24_dtype OUT>
 hipError_t dispatch(const DenseArgs& g, hipStream_t s, const char** kname) {
     const int N = (int)g.N, M = (int)g.M;
     const uint8_t* W = (const uint8_t*)g.W;
     const uint8_t* X = (const uint8_t*)g.X;
-    if (M <= 64) {
+    // the same split as the sparse dispatch: few rows of X on a narrow output
+    // go to the K-splitting decode kernel, everything else to the tile kernels
+    if (M <= 16 || (M <= 64 && (N + 127) / 128 < 128)) {
         const int tiles16 = (N + 15) / 16;
         const int steps = (int)((g.K + DenseOp16<DT>::KSTEP - 1) / DenseOp16<DT>::KSTEP);
         int waves = 16;
@@ -335,15 +198,8 @@ hipError_t dispatch(const DenseArgs& g, hipStream_t s, const char** kname) {
         else if (mt == 2) DENSE_SKINNY(2, 2);
         else DENSE_SKINNY(4, 2);
 #undef DENSE_SKINNY
-    } else if ((int64_t)((N + 255) / 256) * ((M + 255) / 256) >= 192) {
-        return launch_dense_gemm_big(g, s, kname);
     } else {
-        constexpr int FA = 2, FB = 2, BA = 2 * FA * 32, BB = 2 * FB * 32;
-        const int tiles_n = (N + BA - 1) / BA, tiles_m = (M + BB - 1) / BB;
-        if (!g.dry)
-            hipLaunchKernelGGL((dense_tiled<DT, OUT, FA, FB>), dim3(tiles_n * tiles_m), dim3(256), 0, s, W,
-                               X, g.scale_x, g.scale_w, g.Y, N, M, g.K, tiles_n);
-        if (kname) *kname = "dense_tiled_128x128";
+        return launch_dense_gemm_big(g, s, kname);
     }
     return g.dry ? hipSuccess : hipGetLastError();
 }

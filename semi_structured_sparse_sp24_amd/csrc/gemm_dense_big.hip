@@ -1,7 +1,8 @@
-// gemm_dense_big.hip -- dense GEMM baseline Y = X * W^T for large M, built
-// the same way as the large sparse kernel so that the tactic comparison is
-// between kernels of the same construction ("Production 2:4 Structured
-// Sparsity for LLMs", section "Sparse Tactic Audit").
+// gemm_dense_big.hip -- dense GEMM baseline Y = X * W^T for more than 16
+// rows of X, built the same way as the sparse tile kernels (same tile shapes
+// and tile choice) so that the tactic comparison is between kernels of the
+// same construction ("Production 2:4 Structured Sparsity for LLMs", section
+// "Sparse Tactic Audit").  Shown for the 256 x 256 tile:
 //
 //   - tile 256 (W rows) x 256 (X rows); 8 waves in a 4 x 2 grid (two per
 //     SIMD), each owning 64 x 128 = 2 x 4 fragments of v_mfma_f32_32x32x16
@@ -20,11 +21,20 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBA = 256, kBB = 256;
-constexpr int kWA = 4, kWB = 2, kWaves = kWA * kWB, kThreads = 64 * kWaves;
-constexpr int kFA = kBA / 32 / kWA, kFB = kBB / 32 / kWB;   // 32x32 fragments per wave: 2 x 4
-constexpr int kLoads = kBA * 128 / 1024 / kWaves;            // 1 KiB loads per operand and wave: 4
-constexpr int kStage = 256 * 128;   // bytes per operand per stage
+// Tile shapes: BA rows of W x BB rows of X, WA x WB waves, OCC workgroups per CU.
+template <int BA_, int BB_, int WA_, int WB_, int OCC_>
+struct DTile {
+    static constexpr int BA = BA_, BB = BB_, WA = WA_, WB = WB_, OCC = OCC_;
+    static constexpr int WAVES = WA * WB, THREADS = 64 * WAVES;
+    static constexpr int FA = BA / 32 / WA, FB = BB / 32 / WB;    // 32x32 fragments per wave
+    static constexpr int LA = BA * 128 / 1024 / WAVES;            // 1 KiB loads of W per wave and stage
+    static constexpr int LB = BB * 128 / 1024 / WAVES;            // ... of X
+};
+using D256x256 = DTile<256, 256, 4, 2, 1>;
+using D256x128 = DTile<256, 128, 4, 2, 1>;
+using D128x128 = DTile<128, 128, 2, 4, 2>;
+using D256x64 = DTile<256, 64, 4, 2, 1>;
+using D128x64 = DTile<128, 64, 4, 2, 2>;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lgkm0() {
@@ -59,15 +69,18 @@ struct Dense32<SP24_E4M3> {
     }
 };
 
-template <sp24_dtype DT, sp24_dtype OUT>
-__global__ void __launch_bounds__(kThreads, 1)
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
+__global__ void __launch_bounds__(TL::THREADS, TL::OCC)
 dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
           const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K, int tiles_a,
           int tiles_b) {
     using Op = Dense32<DT>;
-    constexpr int LOADS = 2 * kLoads;               // per wave per stage
-    __shared__ __attribute__((aligned(1024))) uint8_t a0s[kStage], a1s[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t b0s[kStage], b1s[kStage];
+    constexpr int kBA = TL::BA, kBB = TL::BB, kWB = TL::WB, kFA = TL::FA, kFB = TL::FB;
+    constexpr int LA = TL::LA, LB = TL::LB;
+    static_assert(LA * TL::WAVES * 1024 == kBA * 128 && LB * TL::WAVES * 1024 == kBB * 128, "whole loads");
+    constexpr int LOADS = LA + LB;                  // per wave per stage
+    __shared__ __attribute__((aligned(1024))) uint8_t a0s[kBA * 128], a1s[kBA * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t b0s[kBB * 128], b1s[kBB * 128];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -90,16 +103,22 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
     const Buf bufW(W, (uint32_t)N * row_bytes);           // rows past N / M read as zeros
     const Buf bufX(X, (uint32_t)M * row_bytes);
 
-    // ---- this wave's loads: kLoads x 1 KiB of W rows and as many of X rows per stage
-    uint32_t ga[kLoads], gb[kLoads];
-    int gc[kLoads];   // byte column of the chunk each lane fetches (for the partial last step)
+    // ---- this wave's loads: LA x 1 KiB of W rows and LB of X rows per stage
+    // (8 rows per load; lane l fetches the chunk that the row's XOR swizzle
+    // puts in slot l & 7)
+    uint32_t ga[LA], gb[LB];
+    int ca[LA], cb[LB];   // byte column of the chunk each lane fetches (for the partial last step)
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        const int row = 8 * (kLoads * wave + j) + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        gc[j] = 16 * c;
-        ga[j] = (uint32_t)(a0 + row) * row_bytes + 16 * c;
-        gb[j] = (uint32_t)(b0 + row) * row_bytes + 16 * c;
+    for (int j = 0; j < LA; ++j) {
+        const int row = 8 * (LA * wave + j) + (lane >> 3);
+        ca[j] = 16 * ((lane & 7) ^ ((row >> 1) & 7));
+        ga[j] = (uint32_t)(a0 + row) * row_bytes + ca[j];
+    }
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        const int row = 8 * (LB * wave + j) + (lane >> 3);
+        cb[j] = 16 * ((lane & 7) ^ ((row >> 1) & 7));
+        gb[j] = (uint32_t)(b0 + row) * row_bytes + cb[j];
     }
     const int rot = (int)(((unsigned)group * 13u) % (unsigned)steps);
     auto issue = [&](uint8_t* as, uint8_t* bs, int sl) {
@@ -108,15 +127,15 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
         const bool live = sl < steps;
         const uint32_t so = (uint32_t)s * 128;
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            const bool in = live && so + gc[j] < row_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufW.r, (lds_void*)(as + 1024 * (kLoads * wave + j)), 16,
+        for (int j = 0; j < LA; ++j) {
+            const bool in = live && so + ca[j] < row_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufW.r, (lds_void*)(as + 1024 * (LA * wave + j)), 16,
                                                      (int)(in ? ga[j] : kOOB), (int)(in ? so : 0u), 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            const bool in = live && so + gc[j] < row_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufX.r, (lds_void*)(bs + 1024 * (kLoads * wave + j)), 16,
+        for (int j = 0; j < LB; ++j) {
+            const bool in = live && so + cb[j] < row_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufX.r, (lds_void*)(bs + 1024 * (LB * wave + j)), 16,
                                                      (int)(in ? gb[j] : kOOB), (int)(in ? so : 0u), 0, 0);
         }
     };
@@ -201,18 +220,37 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
     }
 }
 
-template <sp24_dtype DT, sp24_dtype OUT>
-hipError_t launch(const DenseArgs& g, hipStream_t s, const char** kname) {
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
+hipError_t launch_tile(const DenseArgs& g, hipStream_t s, const char** kname, const char* name) {
     const int N = (int)g.N, M = (int)g.M;
-    const int tiles_a = (N + kBA - 1) / kBA, tiles_b = (M + kBB - 1) / kBB;
+    const int tiles_a = (N + TL::BA - 1) / TL::BA, tiles_b = (M + TL::BB - 1) / TL::BB;
     if (kname)
-        *kname = "dense_big_256x256";
+        *kname = name;
     if (g.dry)
         return hipSuccess;
-    hipLaunchKernelGGL((dense_big<DT, OUT>), dim3(tiles_a * tiles_b), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((dense_big<DT, OUT, TL>), dim3(tiles_a * tiles_b), dim3(TL::THREADS), 0, s,
                        (const uint8_t*)g.W, (const uint8_t*)g.X, g.scale_x, g.scale_w, g.Y, N, M, g.K, tiles_a,
                        tiles_b);
     return hipGetLastError();
+}
+
+template <class TL>
+int64_t tiles_of(const DenseArgs& g) {
+    return ((g.N + TL::BA - 1) / TL::BA) * ((g.M + TL::BB - 1) / TL::BB) * TL::OCC;
+}
+
+// The same tile choice as the sparse kernels: the largest tile that keeps
+// most CUs busy (192 workgroups), else the smallest.
+template <sp24_dtype DT, sp24_dtype OUT>
+hipError_t launch(const DenseArgs& g, hipStream_t s, const char** kname) {
+    constexpr int64_t kFill = 192;
+    if (g.M > 64) {
+        if (tiles_of<D256x256>(g) >= kFill) return launch_tile<DT, OUT, D256x256>(g, s, kname, "dense_big_256x256");
+        if (tiles_of<D256x128>(g) >= kFill) return launch_tile<DT, OUT, D256x128>(g, s, kname, "dense_big_256x128");
+        return launch_tile<DT, OUT, D128x128>(g, s, kname, "dense_big_128x128");
+    }
+    if (tiles_of<D256x64>(g) >= kFill) return launch_tile<DT, OUT, D256x64>(g, s, kname, "dense_big_256x64");
+    return launch_tile<DT, OUT, D128x64>(g, s, kname, "dense_big_128x64");
 }
 
 }  // namespace

@@ -64,7 +64,7 @@ struct DenseArgs {
     bool dry = false;        // only report the kernel that would be launched
 };
 hipError_t launch_dense_gemm(const DenseArgs& g, hipStream_t s, const char** kname);
-// The 256 x 256-tile dense kernel for large M (called by launch_dense_gemm).
+// The LDS-staged dense tile kernels (called by launch_dense_gemm).
 hipError_t launch_dense_gemm_big(const DenseArgs& g, hipStream_t s, const char** kname);
 
 }  // namespace sp24

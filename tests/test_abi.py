@@ -112,6 +112,8 @@ def test_gemm_kernel_names_follow_the_dispatch():
     assert k(True, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "sp24_big_128x128"
     assert k(True, sp.SPARSE_W, bf, bf, 64, 28672, 4096) == "sp24_big_128x64"
     assert k(False, sp.SPARSE_W, bf, bf, 8192, 4096, 4096) == "dense_big_256x256"
+    assert k(False, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "dense_big_128x128"
+    assert k(False, sp.SPARSE_W, bf, bf, 64, 28672, 4096) == "dense_big_128x64"
     # rejected shapes and degenerate ones
     assert k(True, sp.SPARSE_W, bf, bf, 4, 4096, 96) is None
     assert k(False, sp.SPARSE_W, bf, bf, 4, 4096, 100) is None

@@ -157,6 +157,24 @@ def test_skinny_variants_exact(dt, M, N, K, kernel):
     assert np.array_equal(Y, R)
 
 
+DENSE_FEW = [(40, 17000, 704, "dense_big_128x64"), (17, 61500, 200, "dense_big_256x64"),
+             (64, 190, 704, "dense_skinny_m4"), (20, 300, 200, "dense_skinny_m2")]
+
+
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
+@pytest.mark.parametrize("M,N,K,kernel", DENSE_FEW)
+def test_dense_few_rows_exact(dt, M, N, K, kernel):
+    """The dense kernels of the few-row range (tile kernels on wide outputs,
+    the K-splitting kernel otherwise), with a partial last K step, on
+    exact-integer inputs: bitwise equal to the oracle."""
+    K = K if dt != oracle.E4M3 else 2 * K
+    ttype = {oracle.BF16: torch.bfloat16, oracle.F16: torch.float16, oracle.E4M3: torch.float8_e4m3fn}[dt]
+    assert sp.gemm_kernel(False, sp.SPARSE_W, ttype, torch.float32, M, N, K) == kernel
+    say("dense few", kernel, dt, M, N, K)
+    Y, R, _ = _dense(dt, oracle.F32, M, N, K, seed=M * 11 + N, integer=True)
+    assert np.array_equal(Y, R)
+
+
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.E4M3])
 @pytest.mark.parametrize("M,N,K", [(3, 40, 96), (16, 17, 200), (100, 70, 112), (130, 129, 1040)])
 def test_dense_accepts_k_the_sparse_path_rejects(dt, M, N, K):
