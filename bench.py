@@ -405,7 +405,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_per_launch(kname, workload),
                 "kernel": kname, "launches": k["n"], "flops_per_launch": round(k["flops"] / k["n"]),
-                "avg_launch_us": round(avg_us, 3)}
+                "bytes_per_launch": round(k["bytes"] / k["n"]), "avg_launch_us": round(avg_us, 3)}
     all_t = sum(v["t"] for v in per_kernel.values())
     roof["kernels"] = {n: {"launches": v["n"], "avg_launch_us": round(v["t"] / v["n"], 3),
                            "share": round(v["t"] / all_t, 3)} for n, v in per_kernel.items()}

@@ -92,7 +92,7 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     const int per_xcd = (nwg + 7) >> 3, full = nwg & 7 ? (nwg & 7) : 8;
     const int t = xcd < full ? xcd * per_xcd + local : full * per_xcd + (xcd - full) * (per_xcd - 1) + local;
-    constexpr int G = 4;
+    constexpr int G = 8;
     const int group = t / (G * tiles_b), within = t - group * G * tiles_b;
     const int g_rows = min(G, tiles_a - group * G);
     const int ta = group * G + within % g_rows, tb = within / g_rows;
