@@ -6,8 +6,8 @@ A step is one pass of the whole hot path over the workload's synthetic,
 seeded operands: for every weight shape, prune+compress the weight (or, for
 the online workload, the activation), decompress it (the dense pruned weight
 the fallback uses), then for every M the sparse GEMM and the dense GEMM on
-the same shapes.  Each of these runs as a chain of launches (about 1.5 ms of
-work) captured in a HIP graph and timed with HIP events on the stream it runs
+the same shapes.  Each of these runs as a chain of launches (the same count
+for every case, about 1.5 ms of work for the fastest) captured in a HIP graph and timed with HIP events on the stream it runs
 on (time per launch = chain time / launches).  HBM-bound workloads run "cold": the launches of a
 chain cycle through copies of the weights totalling 640 MiB, so every launch
 reads its operands from HBM as successive layers do; compute-bound ones run
@@ -93,15 +93,18 @@ def traffic_per_launch(kernel, workload):
 # on one copy.
 COLD_BYTES = 640 << 20
 MAX_COPIES = 64
-# A chain runs for about this long, so that the fixed cost of starting a graph (~20 us) stays a
-# small part of the bracketed time.
+# The shortest chain of a workload runs for about this long, so that the fixed cost of starting a
+# graph (~20 us) stays a small part of the bracketed time.  Every GEMM chain of a workload has the
+# same length (and every compress chain likewise): a step holds one launch of each case, so the
+# per-launch averages of a kernel -- and the profiler's, over the same launches -- weight the cases
+# equally, as one step does.  (Chain i of a cold case uses copy i % copies; a copy is reused only
+# after every other copy, more than 640 MiB later.)
 CHAIN_US = 1500.0
 
 
-def chain_length(est_us, copies):
-    """Launches in a chain: about CHAIN_US of work, at least 8, a whole number of passes over the copies."""
-    n = int(min(1024, max(8, -(-CHAIN_US // max(est_us, 1.0)))))
-    return -(-n // copies) * copies
+def chain_length(est_us_list):
+    """Launches per chain for a set of cases: CHAIN_US of work for the fastest, 8 to 256."""
+    return int(min(256, max(8, -(-CHAIN_US // max(min(est_us_list), 1.0)))))
 
 
 def est_us(nbytes, flops):
@@ -151,35 +154,38 @@ def chains(workload, cases):
     """The step as an ordered list of (key, launches, fn): fn(i) issues launch i of the chain."""
     w = inputs.WORKLOADS[workload]
     eb = inputs.ELEM_BYTES[w["dtype"]]
+    Lg = chain_length([est_us((c["N"] * c["K"] + it["M"] * c["K"]) * eb, 2.0 * it["M"] * c["N"] * c["K"])
+                       for c in cases for it in c["ms"]])
+    if workload == "online":
+        Lc = chain_length([est_us(it["M"] * c["K"] * eb * 1.625, 0) for c in cases for it in c["ms"]])
+    else:
+        Lc = chain_length([est_us(c["N"] * c["K"] * eb * 1.625, 0) for c in cases])
     out = []
     for c in cases:
         N, K, cp = c["N"], c["K"], c["copies"]
-        nc = len(cp)
         pick = lambda i, cp=cp: cp[i % len(cp)]
         if workload != "online":
-            L = chain_length(est_us(N * K * eb * 1.625, 0), nc)
-            out.append((("compress", c["s"]), L,
+            out.append((("compress", c["s"]), Lc,
                         lambda i, pick=pick: sp.prune_compress(pick(i)["W"], values=pick(i)["v"], meta=pick(i)["m"])))
-            out.append((("decompress", c["s"]), L,
+            out.append((("decompress", c["s"]), Lc,
                         lambda i, pick=pick, K=K: sp.decompress(pick(i)["v"], pick(i)["m"], K, out=pick(i)["Wp"])))
         for it in c["ms"]:
             M, key = it["M"], (c["s"], it["j"])
-            L = chain_length(est_us((N * K + M * K) * eb, 2.0 * M * N * K), nc)
             if workload == "online":
                 # the activation is the sparse operand: prune+compress it on every call
                 W = cp[0]["W"]
-                out.append((("compress",) + key, chain_length(est_us(M * K * eb * 1.625, 0), 1),
+                out.append((("compress",) + key, Lc,
                             lambda i, it=it: sp.prune_compress(it["X"], values=it["xv"], meta=it["xm"])))
-                out.append((("sparse",) + key, L,
+                out.append((("sparse",) + key, Lg,
                             lambda i, it=it, W=W, M=M, N=N, K=K:
                             sp.sp24_gemm(sp.SPARSE_X, it["xv"], it["xm"], W, M, N, K, out=it["Y"])))
-                out.append((("dense",) + key, L, lambda i, it=it, W=W: sp.dense_gemm(it["X"], W, out=it["Yd"])))
+                out.append((("dense",) + key, Lg, lambda i, it=it, W=W: sp.dense_gemm(it["X"], W, out=it["Yd"])))
                 continue
-            out.append((("sparse",) + key, L,
+            out.append((("sparse",) + key, Lg,
                         lambda i, it=it, pick=pick, M=M, N=N, K=K, c=c:
                         sp.sp24_gemm(sp.SPARSE_W, pick(i)["v"], pick(i)["m"], it["X"], M, N, K,
                                      scale_x=it["sx"], scale_w=c["sw"], out=it["Y"])))
-            out.append((("dense",) + key, L,
+            out.append((("dense",) + key, Lg,
                         lambda i, it=it, pick=pick, c=c:
                         sp.dense_gemm(it["X"], pick(i)["Wp"], scale_x=it["sx"], scale_w=c["sw"], out=it["Yd"])))
     return out
@@ -372,7 +378,8 @@ def main():
 
     # roofline of the dominant kernel: the sparse GEMM kernel (by name, as the dispatch picks it per
     # shape) with the largest share of the step's sparse GEMM time; achieved = its algorithmic bytes
-    # (HBM-bound decode) or flops (MFMA-bound prefill) per launch / its mean launch duration
+    # (HBM-bound decode) or flops (MFMA-bound prefill) per launch / its mean launch duration, over
+    # all its launches (every case of the kernel has the same number of launches)
     per_kernel = {}
     for c in cases:
         for it in c["ms"]:

@@ -142,24 +142,29 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
     // The rotation keeps metadata blocks aligned (a multiple of T), and is
     // dropped when the step count is not a multiple of T.
     const int rot = steps % T ? 0 : (int)(((unsigned)group * 13u) % (unsigned)(steps / T)) * T;
-    auto issue = [&](uint8_t* as, uint8_t* bs, uint8_t* ms, int sl) {
+    auto issue_part = [&](uint8_t* as, uint8_t* bs, uint8_t* ms, int sl, bool do_a, bool do_bm) {
         // step sl of the rotated K loop; steps past the end load nothing useful
         int s = sl + rot;
         s = s >= steps ? s - steps : s;
         const bool live = sl < steps;
         const uint32_t sA = live ? (uint32_t)s * L::A_STEP_BYTES : kOOB;
         const uint32_t sB = live ? (uint32_t)s * L::B_STEP_BYTES : kOOB;
+        if (do_a) {
 #pragma unroll
-        for (int j = 0; j < A_LOADS; ++j)
-            dma16(bufA, as + 1024 * (A_LOADS * wave + j), ga[j], sA);
+            for (int j = 0; j < A_LOADS; ++j)
+                dma16(bufA, as + 1024 * (A_LOADS * wave + j), ga[j], sA);
+        }
+        if (do_bm) {
 #pragma unroll
-        for (int j = 0; j < B_LOADS; ++j)
-            dma16(bufB, bs + 1024 * (B_LOADS * wave + j), gb[j], sB);
-        // the block of steps s .. s + T - 1 (with T = 2 and an odd step count,
-        // the last block's second half is past the row: read, never used)
-        if (ms != nullptr && wave < M_WAVES)
-            dma16(bufM, ms + 1024 * wave, gm, live ? (uint32_t)s * (4 * MWS) : kOOB);
+            for (int j = 0; j < B_LOADS; ++j)
+                dma16(bufB, bs + 1024 * (B_LOADS * wave + j), gb[j], sB);
+            // the block of steps s .. s + T - 1 (with T = 2 and an odd step count,
+            // the last block's second half is past the row: read, never used)
+            if (ms != nullptr && wave < M_WAVES)
+                dma16(bufM, ms + 1024 * wave, gm, live ? (uint32_t)s * (4 * MWS) : kOOB);
+        }
     };
+    auto issue = [&](uint8_t* as, uint8_t* bs, uint8_t* ms, int sl) { issue_part(as, bs, ms, sl, true, true); };
     // before computing step x: this wave's loads of step x have landed when
     // only those of step x + 1 (issued one step later) may be outstanding
     auto wait_step = [&](bool next_has_meta) {
@@ -184,16 +189,18 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
             acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     // u: the step's position within its metadata block
-    auto compute = [&](const uint8_t* as, const uint8_t* bs, const uint8_t* ms, int u) {
-        uint4 fa[kFA];
-        uint32_t fi[kFA];
+    uint4 fa[kFA];
+    uint32_t fi[kFA];
+    auto load_a = [&](const uint8_t* as, const uint8_t* ms, int u) {
 #pragma unroll
         for (int i = 0; i < kFA; ++i) {
             fa[i] = *reinterpret_cast<const uint4*>(as + a_frag + i * 16 * 64);
             fi[i] = *reinterpret_cast<const uint32_t*>(ms + m_frag + 4 * MWS * u + i * 16 * 16) >> msh;
         }
+    };
+    auto compute_cols = [&](const uint8_t* bs, int j0, int j1) {
 #pragma unroll
-        for (int j = 0; j < kFB; ++j) {
+        for (int j = j0; j < j1; ++j) {
             const uint4 fb0 = *reinterpret_cast<const uint4*>(bs + b_frag0 + j * 16 * 128);
             const uint4 fb1 = *reinterpret_cast<const uint4*>(bs + b_frag1 + j * 16 * 128);
 #pragma unroll
@@ -222,8 +229,13 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
             wait_step((u + 1) % T == 0);
             __builtin_amdgcn_s_barrier();
             const int x2 = u + 2;   // issued now: position within the unrolled block
-            issue(as_[x2 % 3], bs_[x2 % 3], x2 % T ? nullptr : ms_[(x2 / T) % 3], s + x2);
-            compute(as_[u % 3], bs_[u % 3], ms_[(u / T) % 3], u % T);
+            uint8_t* const nms = x2 % T ? nullptr : ms_[(x2 / T) % 3];
+            load_a(as_[u % 3], ms_[(u / T) % 3], u % T);
+            // the next stage's loads spread over the step's MFMAs
+            issue_part(as_[x2 % 3], bs_[x2 % 3], nms, s + x2, true, false);
+            compute_cols(bs_[u % 3], 0, kFB / 2);
+            issue_part(as_[x2 % 3], bs_[x2 % 3], nms, s + x2, false, true);
+            compute_cols(bs_[u % 3], kFB / 2, kFB);
         }
     }
     wait_vmcnt<0>();   // drain the (useless) loads of steps past the end
