@@ -198,14 +198,25 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
             fi[i] = *reinterpret_cast<const uint32_t*>(ms + m_frag + 4 * MWS * u + i * 16 * 16) >> msh;
         }
     };
-    auto compute_cols = [&](const uint8_t* bs, int j0, int j1) {
+    // One step's MFMAs, the B fragments read one column ahead of their use
+    // (two register slots), with the next stage's loads issued in two parts
+    // along the way (A loads before the first MFMA, B and metadata halfway).
+    auto compute_step = [&](const uint8_t* bs, auto&& issue_a, auto&& issue_bm) {
+        uint4 b0[2], b1[2];
+        b0[0] = *reinterpret_cast<const uint4*>(bs + b_frag0);
+        b1[0] = *reinterpret_cast<const uint4*>(bs + b_frag1);
+        issue_a();
 #pragma unroll
-        for (int j = j0; j < j1; ++j) {
-            const uint4 fb0 = *reinterpret_cast<const uint4*>(bs + b_frag0 + j * 16 * 128);
-            const uint4 fb1 = *reinterpret_cast<const uint4*>(bs + b_frag1 + j * 16 * 128);
+        for (int j = 0; j < kFB; ++j) {
+            if (j + 1 < kFB) {
+                b0[(j + 1) & 1] = *reinterpret_cast<const uint4*>(bs + b_frag0 + (j + 1) * 16 * 128);
+                b1[(j + 1) & 1] = *reinterpret_cast<const uint4*>(bs + b_frag1 + (j + 1) * 16 * 128);
+            }
+            if (j == kFB / 2)
+                issue_bm();
 #pragma unroll
             for (int i = 0; i < kFA; ++i)
-                acc[i][j] = Op::mma(fa[i], fb0, fb1, fi[i], acc[i][j]);
+                acc[i][j] = Op::mma(fa[i], b0[j & 1], b1[j & 1], fi[i], acc[i][j]);
         }
     };
 
@@ -231,11 +242,8 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
             const int x2 = u + 2;   // issued now: position within the unrolled block
             uint8_t* const nms = x2 % T ? nullptr : ms_[(x2 / T) % 3];
             load_a(as_[u % 3], ms_[(u / T) % 3], u % T);
-            // the next stage's loads spread over the step's MFMAs
-            issue_part(as_[x2 % 3], bs_[x2 % 3], nms, s + x2, true, false);
-            compute_cols(bs_[u % 3], 0, kFB / 2);
-            issue_part(as_[x2 % 3], bs_[x2 % 3], nms, s + x2, false, true);
-            compute_cols(bs_[u % 3], kFB / 2, kFB);
+            compute_step(bs_[u % 3], [&] { issue_part(as_[x2 % 3], bs_[x2 % 3], nms, s + x2, true, false); },
+                         [&] { issue_part(as_[x2 % 3], bs_[x2 % 3], nms, s + x2, false, true); });
         }
     }
     wait_vmcnt<0>();   // drain the (useless) loads of steps past the end
