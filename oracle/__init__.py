@@ -65,6 +65,10 @@ def _load(path=None):
     lib.oracle_prune_compress.argtypes = [i32, i64, i64, vp, i64, vp, vp]
     lib.oracle_decompress.restype = i32
     lib.oracle_decompress.argtypes = [i32, i64, i64, vp, vp, vp, i64]
+    lib.oracle_encode_e4m3.restype = ctypes.c_uint8
+    lib.oracle_encode_e4m3.argtypes = [ctypes.c_double]
+    lib.oracle_quantize_e4m3_rows.restype = i32
+    lib.oracle_quantize_e4m3_rows.argtypes = [i32, i64, i64, vp, i64, vp, vp]
     lib.oracle_gemm.restype = i32
     lib.oracle_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
     lib.oracle_num_threads.restype = i32
@@ -144,6 +148,33 @@ def prune_compress(dt: int, src: np.ndarray):
     if rc != 0:
         raise ValueError(f"oracle_prune_compress rejected dt={dt} shape={src.shape}")
     return values, meta
+
+
+def encode_e4m3(x: np.ndarray) -> np.ndarray:
+    """fp64 values -> OCP e4m3fn codes, round to nearest even, saturating at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    f = _load().oracle_encode_e4m3
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
+
+
+def quantize_e4m3_rows(dt: int, src: np.ndarray):
+    """16-bit rows x K bit patterns -> (e4m3 codes rows x K, fp32 scale per row)."""
+    src = np.ascontiguousarray(src, dtype=_bits_dtype(dt))
+    rows, K = src.shape
+    q = np.empty((rows, K), dtype=np.uint8)
+    scales = np.empty(rows, dtype=np.float32)
+    rc = _load().oracle_quantize_e4m3_rows(dt, rows, K, _ptr(src), K, _ptr(q), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_e4m3_rows rejected dt={dt} shape={src.shape}")
+    return q, scales
+
+
+def quantize_prune_compress(dt: int, src: np.ndarray):
+    """The fused online fp8 path: per-row quantization to e4m3, then 2:4 prune
+    and compress of the codes -> (values rows x K/2, meta, scales)."""
+    q, scales = quantize_e4m3_rows(dt, src)
+    values, meta = prune_compress(E4M3, q)
+    return values, meta, scales
 
 
 def decompress(dt: int, values: np.ndarray, meta: np.ndarray, K: int) -> np.ndarray:

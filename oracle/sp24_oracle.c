@@ -34,7 +34,10 @@
  *     words, unused high nibbles zero;
  *   - dropped positions decompress to +0.0 (bit pattern 0);
  *   - fp8 is OCP E4M3 ("e4m3fn": no Inf, 0x7F/0xFF are NaN, max 448) with one
- *     fp32 scale per row of each operand, applied to the fp64 result.
+ *     fp32 scale per row of each operand, applied to the fp64 result;
+ *   - fused online fp8 path: per-row scale max|x| / 448 and codes e4m3(x / s)
+ *     rounded to nearest even and saturated at 448, both in fp32; pruning
+ *     acts on the codes (quantize first, then prune).
  */
 #include <math.h>
 #include <stdint.h>
@@ -162,6 +165,21 @@ uint16_t oracle_encode_bf16(double x)
     return s | (uint16_t)encode_mag_rne(fabs(x), 7, 127, 254);
 }
 
+/* OCP e4m3fn from fp64, round to nearest even, saturating: magnitudes at or
+ * above the largest finite value 448 give 448 (the format has no infinity);
+ * NaN gives the NaN pattern 0x7F.  Below 448 the rounding can reach 448 but
+ * never the next step up (480, which would need a >= 464). */
+uint8_t oracle_encode_e4m3(double x)
+{
+    if (isnan(x))
+        return 0x7f;
+    uint8_t s = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a >= 448.0)
+        return s | 0x7e;
+    return s | (uint8_t)encode_mag_rne(a, 3, 7, 15);
+}
+
 void oracle_decode_array(int dt, const void *src, int64_t n, double *out)
 {
     for (int64_t i = 0; i < n; ++i)
@@ -282,6 +300,49 @@ int oracle_decompress(int dt, int64_t rows, int64_t K, const void *values,
             int p0 = nibble & 3, p1 = (nibble >> 2) & 3;
             memcpy(row + (4 * g + p0) * eb, vrow + (2 * g) * eb, eb);
             memcpy(row + (4 * g + p1) * eb, vrow + (2 * g + 1) * eb, eb);
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-row fp8 quantization (the fused online path).                   */
+/* ------------------------------------------------------------------ */
+
+/* Rows x K of f16 or bf16 (row stride ld_src elements) to e4m3 codes q
+ * (rows x K, dense) and one fp32 scale per row (the 2:4-versus-quantization
+ * paper, section 2 "Quantization": one scale per row; sections 3.5 and 4.2:
+ * the online operand is quantized, pruned and compressed in one pass).  The
+ * scale maps the row's largest magnitude to the largest finite e4m3 value:
+ * s = max|x| / 448 (s = 1 for an all-zero row), and q = e4m3(x / s).  The
+ * scale and the quotients are computed in fp32 (C float arithmetic, round
+ * to nearest even), not fp64: they decide integer codes, and the GPU takes
+ * the same decisions in the same precision.  Pruning then works on q, so
+ * that the kept values are exactly what the GEMM consumes. */
+int oracle_quantize_e4m3_rows(int dt, int64_t rows, int64_t K, const void *src, int64_t ld_src,
+                              uint8_t *q, float *scales)
+{
+    if (dt != OR_F16 && dt != OR_BF16)
+        return OR_E_ARG;
+    if (rows < 0 || K < 0 || ld_src < K)
+        return OR_E_ARG;
+    int eb = elem_bytes(dt);
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const char *row = (const char *)src + (size_t)(r * ld_src) * eb;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = (float)decode_elem(dt, row, k);     /* exact: every f16/bf16 is a float */
+            float a = fabsf(v);
+            if (a > amax)
+                amax = a;
+        }
+        float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scales[r] = sc;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = (float)decode_elem(dt, row, k);
+            float t = v / sc;
+            q[r * K + k] = oracle_encode_e4m3((double)t);
         }
     }
     return OR_OK;

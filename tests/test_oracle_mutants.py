@@ -10,6 +10,7 @@ import oracle
 from tests import test_oracle_codecs as codecs
 from tests import test_oracle_gemm as gemm
 from tests import test_oracle_prune as prune
+from tests import test_oracle_quant as quant
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "sp24_oracle.c")
 
@@ -29,6 +30,10 @@ MUTANTS = [
     ("weight-scale-dropped", "acc *= (double)scale_w[n];", "acc *= 1.0;"),
     ("k-index-reversed", "acc += x[k] * wrow[k];", "acc += x[k] * wrow[K - 1 - k];"),
     ("last-term-dropped", "for (int64_t k = 0; k < K; ++k)\n                    acc", "for (int64_t k = 0; k < K - 1; ++k)\n                    acc"),
+    ("e4m3-no-saturation", "if (a >= 448.0)\n        return s | 0x7e;", "if (a >= 480.0)\n        return s | 0x7e;"),
+    ("quant-scale-off", "amax / 448.0f", "amax / 447.0f"),
+    ("quant-scale-fp64", "float t = v / sc;", "double t = (double)v / (double)sc;"),
+    ("quant-absmax-signed", "float a = fabsf(v);", "float a = v;"),
 ]
 
 PINS = [
@@ -44,6 +49,10 @@ PINS = [
     lambda: gemm.test_sparse_w_matches_float64_matmul(oracle.E4M3),
     lambda: gemm.test_exact_integer_product(oracle.BF16),
     gemm.test_one_hot_rows_read_back_decompressed_weights,
+    quant.test_encode_e4m3_saturates_and_keeps_nan,
+    lambda: quant.test_quantize_exact_round_trip(oracle.BF16),
+    lambda: quant.test_quantize_row_maximum_and_error_bound(oracle.BF16),
+    quant.test_quantize_decides_codes_in_fp32,
 ]
 
 
