@@ -16,7 +16,7 @@ faster) is selected and the CPU oracle is timed on the host cores.  One JSON
 line is printed.
 
 Workloads (default: decode, the bf16 Llama-3-8B-like decode layers):
-  tiny | decode | prefill | fp8 | online
+  tiny | decode | prefill | fp8 | online | online_fp8
 """
 from __future__ import annotations
 
@@ -92,6 +92,7 @@ def traffic_per_launch(kernel, workload):
 # every launch reads its weights from HBM -- as the layers of a decode step do.  Warm kernels re-run
 # on one copy.
 COLD_BYTES = 640 << 20
+ONLINE = ("online", "online_fp8")   # the activation is the compressed operand, compressed every call
 MAX_COPIES = 64
 # The shortest chain of a workload runs for about this long, so that the fixed cost of starting a
 # graph (~20 us) stays a small part of the bracketed time.  Every GEMM chain of a workload has the
@@ -128,7 +129,7 @@ def build_cases(workload, cold):
         wb, sw = inputs.weight(workload, s)
         W0 = dev(wb, dt)
         shape = {"s": s, "N": N, "K": K, "sw": None if sw is None else torch.from_numpy(sw).cuda(), "ms": []}
-        nc = 1 if workload == "online" else n_copies(N * K * eb // 2 + N * K // 8, cold)
+        nc = 1 if workload in ONLINE else n_copies(N * K * eb // 2 + N * K // 8, cold)
         copies = []
         for i in range(nc):
             W = W0 if i == 0 else W0.clone()
@@ -137,13 +138,19 @@ def build_cases(workload, cold):
         shape["copies"] = copies
         for j, M in enumerate(w["ms"]):
             xb, sx = inputs.activation(workload, s, j)
-            X = dev(xb, dt)
+            X = dev(xb, w.get("act", dt))
             item = {"j": j, "M": M, "X": X, "sx": None if sx is None else torch.from_numpy(sx).cuda(),
                     "Y": torch.empty((M, N), dtype=ytype, device="cuda"),
                     "Yd": torch.empty((M, N), dtype=ytype, device="cuda")}
-            if workload == "online":
+            if workload in ONLINE:
                 item["xv"] = torch.empty((M, K // 2), dtype=TORCH[dt], device="cuda")
                 item["xm"] = torch.empty((M, (K + 31) // 32), dtype=torch.int32, device="cuda")
+            if workload == "online_fp8":
+                # each side quantizes the bf16 activation itself: fused with the prune for the
+                # sparse side, plain for the dense side
+                item["xs"] = torch.empty(M, dtype=torch.float32, device="cuda")
+                item["xq"] = torch.empty((M, K), dtype=TORCH[dt], device="cuda")
+                item["xqs"] = torch.empty(M, dtype=torch.float32, device="cuda")
             shape["ms"].append(item)
         cases.append(shape)
     torch.cuda.synchronize()
@@ -156,21 +163,36 @@ def chains(workload, cases):
     eb = inputs.ELEM_BYTES[w["dtype"]]
     Lg = chain_length([est_us((c["N"] * c["K"] + it["M"] * c["K"]) * eb, 2.0 * it["M"] * c["N"] * c["K"])
                        for c in cases for it in c["ms"]])
-    if workload == "online":
-        Lc = chain_length([est_us(it["M"] * c["K"] * eb * 1.625, 0) for c in cases for it in c["ms"]])
+    if workload in ONLINE:
+        Lc = chain_length([est_us(it["M"] * c["K"] * 2 * 1.625, 0) for c in cases for it in c["ms"]])
     else:
         Lc = chain_length([est_us(c["N"] * c["K"] * eb * 1.625, 0) for c in cases])
     out = []
     for c in cases:
         N, K, cp = c["N"], c["K"], c["copies"]
         pick = lambda i, cp=cp: cp[i % len(cp)]
-        if workload != "online":
+        if workload not in ONLINE:
             out.append((("compress", c["s"]), Lc,
                         lambda i, pick=pick: sp.prune_compress(pick(i)["W"], values=pick(i)["v"], meta=pick(i)["m"])))
             out.append((("decompress", c["s"]), Lc,
                         lambda i, pick=pick, K=K: sp.decompress(pick(i)["v"], pick(i)["m"], K, out=pick(i)["Wp"])))
         for it in c["ms"]:
             M, key = it["M"], (c["s"], it["j"])
+            if workload == "online_fp8":
+                W, sw = cp[0]["W"], c["sw"]
+                out.append((("compress",) + key, Lc,
+                            lambda i, it=it: sp.quantize_prune_compress(it["X"], values=it["xv"], meta=it["xm"],
+                                                                        scales=it["xs"])))
+                out.append((("sparse",) + key, Lg,
+                            lambda i, it=it, W=W, sw=sw, M=M, N=N, K=K:
+                            sp.sp24_gemm(sp.SPARSE_X, it["xv"], it["xm"], W, M, N, K, scale_x=it["xs"],
+                                         scale_w=sw, out=it["Y"])))
+                out.append((("prep",) + key, Lc,
+                            lambda i, it=it: sp.quantize_e4m3(it["X"], out=it["xq"], scales=it["xqs"])))
+                out.append((("dense",) + key, Lg,
+                            lambda i, it=it, W=W, sw=sw: sp.dense_gemm(it["xq"], W, scale_x=it["xqs"], scale_w=sw,
+                                                                       out=it["Yd"])))
+                continue
             if workload == "online":
                 # the activation is the sparse operand: prune+compress it on every call
                 W = cp[0]["W"]
@@ -244,7 +266,7 @@ def cpu_baseline(workload, budget_s):
     for s, (N, K) in enumerate(w["shapes"]):
         wb, sw = inputs.weight(workload, s)
         wv = wm = None
-        if workload != "online":
+        if workload not in ONLINE:
             wv, wm = oracle.prune_compress(dt, wb)
         for j, M in enumerate(w["ms"]):
             xb, sx = inputs.activation(workload, s, j)
@@ -253,6 +275,8 @@ def cpu_baseline(workload, budget_s):
             xv = xm = None
             if workload == "online":
                 xv, xm = oracle.prune_compress(dt, xb)
+            elif workload == "online_fp8":
+                xv, xm, sx = oracle.quantize_prune_compress(w["act"], xb)
             prepared.append((N, K, M, rows, mrows, wb, sw, wv, wm, xb, sx, xv, xm))
     flops = 0.0
     secs = 0.0
@@ -261,8 +285,8 @@ def cpu_baseline(workload, budget_s):
     while secs < budget_s:
         for (N, K, M, rows, mrows, wb, sw, wv, wm, xb, sx, xv, xm) in prepared:
             t0 = time.perf_counter()
-            if workload == "online":
-                oracle.gemm(dt, M, N, K, x_vals=xv, x_meta=xm, w=wb, mrows=mrows)
+            if workload in ONLINE:
+                oracle.gemm(dt, M, N, K, x_vals=xv, x_meta=xm, w=wb, scale_x=sx, scale_w=sw, mrows=mrows)
             else:
                 oracle.gemm(dt, M, N, K, x=xb, w_vals=wv, w_meta=wm, scale_x=sx, scale_w=sw, mrows=mrows)
             secs += time.perf_counter() - t0
@@ -344,7 +368,7 @@ def main():
             key = (c["s"], it["j"])
             ts = times[("sparse",) + key]
             td = times[("dense",) + key]
-            sparse_rows = M if workload == "online" else N
+            sparse_rows = M if workload in ONLINE else N
             sb = sparse_gemm_bytes(M, N, K, eb, out_eb, sparse_rows, scales)
             db = dense_gemm_bytes(M, N, K, eb, out_eb, scales)
             fl = 2.0 * M * N * K
@@ -355,19 +379,24 @@ def main():
                    "sparse_GBps": round(sb / tsm / 1e3, 1), "dense_GBps": round(db / tdm / 1e3, 1),
                    "sparse_hbm_frac": round(sb / tsm / 1e3 / HBM_PEAK_GBPS, 3),
                    "sparse_mfma_frac": round(fl / tsm / 1e6 / SPARSE_PEAK_TFLOPS[dt], 3)}
-            if workload == "online":
+            if workload in ONLINE:
                 tc = float(np.median(times[("compress",) + key]))
+                tp = float(np.median(times[("prep",) + key])) if workload == "online_fp8" else 0.0
                 row["t_compress_us"] = round(tc, 2)
-                row["speedup_incl_compress"] = round(tdm / (tc + tsm), 3)
+                if workload == "online_fp8":
+                    row["t_dense_quantize_us"] = round(tp, 2)
+                row["speedup_incl_compress"] = round((tp + tdm) / (tc + tsm), 3)
                 tot["compress_t"] += sum(times[("compress",) + key])
-                tot["compress_bytes"] += compress_bytes(M, K, eb) * len(times[("compress",) + key])
+                cb = (M * K * 2 + M * K // 2 + M * K // 8 + 4 * M) if workload == "online_fp8" \
+                    else compress_bytes(M, K, eb)
+                tot["compress_bytes"] += cb * len(times[("compress",) + key])
             rows.append(row)
             tot["sparse_t"] += sum(ts)
             tot["dense_t"] += sum(td)
             tot["flops"] += fl * len(ts)
             tot["sparse_bytes"] += sb * len(ts)
             tot["sparse_launches"] += len(ts)
-        if workload != "online":
+        if workload not in ONLINE:
             tcs = times[("compress", c["s"])]
             tot["compress_t"] += sum(tcs)
             tot["compress_bytes"] += compress_bytes(N, K, eb) * len(tcs)
@@ -384,11 +413,11 @@ def main():
     for c in cases:
         for it in c["ms"]:
             M, N, K = it["M"], c["N"], c["K"]
-            which = sp.SPARSE_X if workload == "online" else sp.SPARSE_W
+            which = sp.SPARSE_X if workload in ONLINE else sp.SPARSE_W
             name = sp.gemm_kernel(True, which, TORCH[dt], it["Y"].dtype, M, N, K)
             key = ("sparse", c["s"], it["j"])
             ts, L = times[key], runner.length[key]       # per-launch means of each step; chain length
-            sparse_rows = M if workload == "online" else N
+            sparse_rows = M if workload in ONLINE else N
             k = per_kernel.setdefault(name, {"t": 0.0, "n": 0, "bytes": 0.0, "flops": 0.0})
             # weighted by launches, as a profiler's per-kernel average is
             k["t"] += sum(ts) * L
@@ -422,7 +451,13 @@ def main():
         for c in cases:
             for it in c["ms"]:
                 M, N, K = it["M"], c["N"], c["K"]
-                if workload == "online":
+                if workload == "online_fp8":
+                    # both sides quantize; the tactic compares the rest: prune+compress of the codes
+                    # and the sparse GEMM against the dense GEMM on the codes
+                    rec = sp.select_tactic(sp.SPARSE_X, it["xv"], it["xm"], c["copies"][0]["W"], it["xq"], M, N, K,
+                                           scale_x=it["xqs"], scale_w=c["sw"], y_scratch=it["Y"], warmup=3,
+                                           reps=10)
+                elif workload == "online":
                     rec = sp.select_tactic(sp.SPARSE_X, it["xv"], it["xm"], c["copies"][0]["W"], it["X"], M, N, K,
                                            y_scratch=it["Y"], warmup=3, reps=10)
                 else:

@@ -122,6 +122,40 @@ sp24_status sp24_decompress(sp24_dtype dt, int64_t rows, int64_t K,
                             void *dst, int64_t ld_dst, hipStream_t stream);
 
 /*
+ * The fused online fp8 path for a dynamic operand (the 2:4-versus-quantization
+ * paper, sections 3.5 "Measuring speed" and 4.2 "Speed": quantize, prune and
+ * compress in one pass that reads the operand once and writes the kept values
+ * and their indices once; section 2 "Quantization": one scale per row).
+ * Per row r of the f16 / bf16 source:
+ *   scales[r] = max|x| / 448 in fp32 (1 for an all-zero row);
+ *   codes     = e4m3fn(x / scales[r]), the quotient in fp32, rounded to
+ *               nearest even and saturated at 448;
+ *   then the magnitude 2:4 prune and compress of the codes, exactly as
+ *   sp24_prune_compress does for SP24_E4M3 input.
+ *   src_dt    SP24_F16 or SP24_BF16
+ *   rows, K   rows >= 0; K % 32 == 0 (whole metadata words), else SP24_E_ALIGN
+ *   src       rows x K, row stride ld_src elements (ld_src >= K, ld_src % 8 == 0)
+ *   values    out: rows x K/2 e4m3 bytes;  meta  out: rows x K/32 words
+ *   scales    out: rows fp32
+ *   Pointers 16-byte aligned (scales 4-byte).  The outputs feed
+ *   sp24_gemm(SP24_SPARSE_X, SP24_E4M3, ..., scale_x = scales, ...).
+ */
+sp24_status sp24_quantize_prune_compress(sp24_dtype src_dt, int64_t rows, int64_t K,
+                                         const void *src, int64_t ld_src,
+                                         void *values, uint32_t *meta, float *scales,
+                                         hipStream_t stream);
+
+/*
+ * The same per-row e4m3 quantization without the prune: every code, rows x K
+ * e4m3 bytes into `dst` (row stride K), one fp32 scale per row.  The dense
+ * side of the online fp8 comparison: each side pays for producing its own
+ * input.  Same dtypes, sizes, alignment and errors as above.
+ */
+sp24_status sp24_quantize_e4m3(sp24_dtype src_dt, int64_t rows, int64_t K,
+                               const void *src, int64_t ld_src, void *dst, float *scales,
+                               hipStream_t stream);
+
+/*
  * Sparse x dense GEMM, Y = X * W^T (the paper's section 2 "Sparse tensor
  * cores": the compressed first operand and its indices select the matching
  * elements of the dense operand).

@@ -13,6 +13,8 @@ PyTorch fallback: if the library is missing, every call raises.
   select_tactic(...)           -> per-shape sparse-or-dense record
   tactic_decide(...)           -> the decision rule on given timings (host only)
   gemm_kernel(...)             -> name of the kernel a GEMM call would launch (host only)
+  quantize_prune_compress(x)   -> (values e4m3, meta, scales): fused online fp8 path
+  quantize_e4m3(x)             -> (codes e4m3, scales): the dense side's quantization
 """
 from __future__ import annotations
 
@@ -59,6 +61,8 @@ SIGNATURES = {
     "sp24_tactic_decide": (_i32, [_i32, ctypes.POINTER(_dbl), _i32, ctypes.POINTER(_dbl), _i32,
                                   ctypes.POINTER(Tactic)]),
     "sp24_gemm_kernel": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i64, _i64, _i64]),
+    "sp24_quantize_prune_compress": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp]),
+    "sp24_quantize_e4m3": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -125,6 +129,37 @@ def prune_compress(dense: torch.Tensor, values=None, meta=None):
                                    _ptr(meta), _stream(dense.device))
     _check("sp24_prune_compress", st)
     return values, meta
+
+
+def quantize_prune_compress(x: torch.Tensor, values=None, meta=None, scales=None):
+    """Per-row e4m3 quantization fused with the 2:4 prune and compress:
+    (values rows x K/2 e4m3, meta rows x K/32 int32, scales rows fp32)."""
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
+    rows, K = x.shape
+    if values is None:
+        values = torch.empty((rows, K // 2), dtype=torch.float8_e4m3fn, device=x.device)
+    if meta is None:
+        meta = torch.empty((rows, (K + 31) // 32), dtype=torch.int32, device=x.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    st = lib().sp24_quantize_prune_compress(_code(x), rows, K, _ptr(x), x.stride(0), _ptr(values), _ptr(meta),
+                                            _ptr(scales), _stream(x.device))
+    _check("sp24_quantize_prune_compress", st)
+    return values, meta, scales
+
+
+def quantize_e4m3(x: torch.Tensor, out=None, scales=None):
+    """Per-row e4m3 quantization: (codes rows x K e4m3, scales rows fp32)."""
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
+    rows, K = x.shape
+    if out is None:
+        out = torch.empty((rows, K), dtype=torch.float8_e4m3fn, device=x.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    st = lib().sp24_quantize_e4m3(_code(x), rows, K, _ptr(x), x.stride(0), _ptr(out), _ptr(scales),
+                                  _stream(x.device))
+    _check("sp24_quantize_e4m3", st)
+    return out, scales
 
 
 def decompress(values: torch.Tensor, meta: torch.Tensor, K: int, out=None):

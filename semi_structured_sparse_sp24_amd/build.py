@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsp24.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "compress.hip", "gemm_sparse.hip", "gemm_sparse_big.hip",
+SOURCES = ["api.hip", "compress.hip", "quantize.hip", "gemm_sparse.hip", "gemm_sparse_big.hip",
            "gemm_dense.hip", "gemm_dense_big.hip"]
 
 CFLAGS = [

@@ -147,6 +147,34 @@ SP24_API sp24_status sp24_decompress(sp24_dtype dt, int64_t rows, int64_t K, con
                ? SP24_OK : SP24_E_HIP;
 }
 
+static sp24_status quantize_impl(sp24_dtype dt, int64_t rows, int64_t K, const void* src, int64_t ld_src,
+                                 void* out, uint32_t* meta, float* scales, bool prune, hipStream_t stream) {
+    if (dt != SP24_F16 && dt != SP24_BF16)
+        return SP24_E_DTYPE;
+    if (rows < 0 || K < 0 || ld_src < K)
+        return SP24_E_SHAPE;
+    if (rows == 0 || K == 0)
+        return SP24_OK;
+    if (!src || !out || !scales || (prune && !meta))
+        return SP24_E_NULL;
+    if (K % 32 != 0 || ld_src % 8 != 0 || !aligned16(src) || !aligned16(out) || (prune && !aligned16(meta)) ||
+        ((uintptr_t)scales & 3u))
+        return SP24_E_ALIGN;
+    return launch_quantize_e4m3(dt, rows, K, src, ld_src, out, prune ? meta : nullptr, scales, stream) == hipSuccess
+               ? SP24_OK : SP24_E_HIP;
+}
+
+SP24_API sp24_status sp24_quantize_prune_compress(sp24_dtype src_dt, int64_t rows, int64_t K, const void* src,
+                                                  int64_t ld_src, void* values, uint32_t* meta, float* scales,
+                                                  hipStream_t stream) {
+    return quantize_impl(src_dt, rows, K, src, ld_src, values, meta, scales, true, stream);
+}
+
+SP24_API sp24_status sp24_quantize_e4m3(sp24_dtype src_dt, int64_t rows, int64_t K, const void* src,
+                                        int64_t ld_src, void* dst, float* scales, hipStream_t stream) {
+    return quantize_impl(src_dt, rows, K, src, ld_src, dst, nullptr, scales, false, stream);
+}
+
 static sp24_status gemm_impl(sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt, int64_t M,
                              int64_t N, int64_t K, const void* values, const uint32_t* meta,
                              const void* dense, const float* scale_x, const float* scale_w, void* Y,

@@ -1,0 +1,331 @@
+// quantize.hip -- per-row fp8 (e4m3) quantization of a 16-bit operand, fused
+// with the magnitude 2:4 prune and compress for dynamic activations.
+//
+// The online path of the 2:4-versus-quantization paper (section 3.5, "Measuring
+// speed", and 4.2, "Speed"): the activation is quantized, pruned and compressed
+// in one pass that reads it once and writes the kept values and their indices
+// once; one scale per row (section 2, "Quantization").  Per row:
+//   s = max|x| / 448   (1 for an all-zero row; a NaN does not count), in fp32;
+//   q = e4m3(x / s)    x / s in fp32 (correctly rounded division), then round
+//                      to nearest even to OCP e4m3fn, saturating at 448;
+//   prune: in every group of four codes keep the two of largest magnitude
+//   (ties to the lower index) -- the codes are what the GEMM consumes, so the
+//   selection is made on them.
+// The plain variant writes all codes (the dense fp8 GEMM's input).
+//
+// A row belongs to one, two or four waves (L = 64, 128 or 256 lanes, the
+// fewest that hold it in registers).  Lane t takes the 16-element chunks
+// t, t + L, ... (two 16-byte loads each) and keeps them: the row is read from
+// memory once, its maximum found with a wave reduction (and LDS words across
+// waves), and the codes formed from the registers.  With one wave per row
+// (K <= 4096) a workgroup holds four rows and no barrier.  Rows longer than
+// 256 * kMaxChunks chunks are taken in rounds and read twice.
+//
+// Codes without the division.  With y = 1/s (correctly rounded, once per row,
+// then lowered by 2^-21 relative) t = x * y lies below x / s in magnitude, by
+// 5 to 11 units of 2^-24 relative; so the fp32 quotient q lies strictly above
+// t and at most 23 fp32 ulps of t beyond it, and |t| < 448.  Rounding is
+// monotone: when t and the fp32 value 32 ulps beyond it (its bit pattern + 32)
+// convert to the same e4m3 code, so does every value between them, q
+// included, and the hardware conversion of t is the code.  Otherwise (about
+// one element in 3 * 10^4 for Gaussian rows) the four elements of that word
+// take the exact division and the bitwise encoder, as do rows holding an
+// infinity or a NaN, or whose scale is below the fp32 normals.
+#include "sp24_internal.h"
+
+namespace sp24 {
+namespace {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;     // four waves per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxChunks = 8;     // 16-element chunks a lane holds at once
+
+__device__ __forceinline__ float bits_to_float(uint32_t h, sp24_dtype dt) {
+    if (dt == SP24_BF16)
+        return __builtin_bit_cast(float, h << 16);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// fp32 -> e4m3fn code by its bit pattern: round to nearest even, saturating
+// at 448 (0x7e); NaN -> 0x7f.  The exact path for the few values the
+// conversion instruction is not trusted with.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t mag = u & 0x7fffffffu;
+    if (mag > 0x7f800000u)
+        return 0x7fu;
+    if (mag >= 0x43e00000u)                     // |v| >= 448
+        return sign | 0x7eu;
+    const int e = (int)(mag >> 23) - 127;
+    uint32_t code;
+    if (e < -6) {
+        // below the smallest normal: a multiple of 2^-9, rounded to even
+        const float t = __builtin_bit_cast(float, mag) * 512.0f;   // exact scaling
+        code = (uint32_t)__builtin_rintf(t);                        // 0 .. 8 (8 = smallest normal)
+    } else {
+        const uint32_t man = mag & 0x7fffffu;
+        uint32_t keep = man >> 20;
+        const uint32_t rest = man & 0xfffffu;
+        keep += (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ? 1u : 0u;
+        code = ((uint32_t)(e + 7) << 3) + keep;                     // a carry moves to the exponent
+    }
+    return sign | code;
+}
+
+// The e4m3 codes of four fp32 values, element order from the low byte.
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+__device__ __forceinline__ float above(float t) {   // 32 ulps further from zero
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, t) + 32u);
+}
+
+__device__ __forceinline__ uint32_t pmax(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pmin(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// The 2:4 selection on two groups of four codes at once (group A in the low
+// 16-bit half, group B in the high half).  Key of position i: code magnitude
+// in the high byte, 3 - i in the low byte, so the larger key is the larger
+// magnitude and, among equals, the lower index.  Returns the kept positions
+// p0 < p1 of each group, one per half (p0 in `lo`, p1 in `hi`).
+__device__ __forceinline__ void top2_pair(uint32_t A, uint32_t B, uint32_t& lo, uint32_t& hi) {
+    uint32_t k[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // bytes: 0, A.byte i, 0, B.byte i   (selector 12 gives a zero byte)
+        const uint32_t p = __builtin_amdgcn_perm(B, A, 0x000c000cu | ((uint32_t)i << 8) | ((uint32_t)(4 + i) << 24));
+        k[i] = (p & 0x7f007f00u) | ((uint32_t)(3 - i) * 0x00010001u);
+    }
+    const uint32_t hi01 = pmax(k[0], k[1]), lo01 = pmin(k[0], k[1]);
+    const uint32_t hi23 = pmax(k[2], k[3]), lo23 = pmin(k[2], k[3]);
+    const uint32_t first = pmax(hi01, hi23);
+    const uint32_t second = pmax(pmin(hi01, hi23), pmax(lo01, lo23));
+    const uint32_t pa = (first & 0x00030003u) ^ 0x00030003u;     // 3 - (3 - i)
+    const uint32_t pb = (second & 0x00030003u) ^ 0x00030003u;
+    lo = pmin(pa, pb);
+    hi = pmax(pa, pb);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+// Maximum over the WPR waves of one row; every lane of the row gets it.
+// `slot` picks the LDS words, so a second reduction needs no barrier before
+// its writes.
+template <int WPR>
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v, uint32_t (*red)[kWaves], int slot) {
+    v = wave_max_u32(v);
+    if (WPR == 1)
+        return v;
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+        red[slot][wave] = v;
+    __syncthreads();
+    const int w0 = wave / WPR * WPR;
+    uint32_t m = red[slot][w0];
+#pragma unroll
+    for (int i = 1; i < WPR; ++i)
+        m = max(m, red[slot][w0 + i]);
+    return m;
+}
+
+// One row per WPR waves (4 / WPR rows per workgroup), CH chunks per lane and
+// round.  PRUNE: write kept codes + metadata; else write every code.
+template <sp24_dtype DT, bool PRUNE, int WPR, int CH>
+__global__ void __launch_bounds__(kThreads)
+quantize_rows(const uint8_t* __restrict__ src, int64_t ld_bytes, int64_t rows, int64_t K,
+              uint8_t* __restrict__ out, uint8_t* __restrict__ meta, float* __restrict__ scales) {
+    constexpr int kLanes = 64 * WPR;                 // lanes per row
+    __shared__ uint32_t red[2][kWaves];
+    const int lr = threadIdx.x % kLanes;
+    const int64_t row = (int64_t)blockIdx.x * (kWaves / WPR) + threadIdx.x / kLanes;
+    // a row of waves past the end: with one wave per row it leaves, else it
+    // still takes part in the workgroup's barriers
+    if (WPR == 1 && row >= rows)
+        return;
+    const bool live = row < rows;
+    const uint8_t* r = src + row * ld_bytes;
+    const int64_t chunks = live ? K / 16 : 0;
+    constexpr int64_t kRound = (int64_t)kLanes * CH;
+    // fewer than kMaxChunks per lane: the launch chose CH so that one round covers the row
+    const int rounds = CH < kMaxChunks ? 1 : (int)((K / 16 + kRound - 1) / kRound);
+    constexpr uint32_t kInf = DT == SP24_BF16 ? 0x7f80u : 0x7c00u;   // magnitude bits of +inf
+
+    uint4 a[CH], b[CH];
+    auto load = [&](int rd) {
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int64_t c = rd * kRound + u * kLanes + lr;
+            const bool in = c < chunks;
+            a[u] = in ? *reinterpret_cast<const uint4*>(r + 32 * c) : make_uint4(0, 0, 0, 0);
+            b[u] = in ? *reinterpret_cast<const uint4*>(r + 32 * c + 16) : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    // ---- max |x| as magnitude bits (ordered like the values), two halves per word
+    uint32_t mx = 0;
+    for (int rd = 0; rd < rounds; ++rd) {
+        load(rd);
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const uint32_t w[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                mx = pmax(mx, w[i] & 0x7fff7fffu);
+        }
+    }
+    const uint32_t amax_raw = row_max_u32<WPR>(max(mx & 0xffffu, mx >> 16), red, 0);
+    uint32_t amax = amax_raw;
+    bool has_nan = amax_raw > kInf;
+    if (WPR > 1)
+        has_nan = __syncthreads_or(has_nan);          // the branch holds a barrier: decide it per workgroup
+    if (has_nan) {
+        // a NaN is in the row: the maximum is taken over the other elements
+        uint32_t m = 0;
+        for (int64_t c = lr; c < chunks; c += kLanes) {
+            const uint4 p = *reinterpret_cast<const uint4*>(r + 32 * c);
+            const uint4 q = *reinterpret_cast<const uint4*>(r + 32 * c + 16);
+            const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t l = w[i] & 0x7fffu, h = (w[i] >> 16) & 0x7fffu;
+                m = max(m, l <= kInf ? l : 0u);
+                m = max(m, h <= kInf ? h : 0u);
+            }
+        }
+        amax = row_max_u32<WPR>(m, red, 1);
+    }
+    const float s = amax ? __fdiv_rn(bits_to_float(amax, DT), 448.0f) : 1.0f;
+    const float y = __fdiv_rn(1.0f, s) * (1.0f - 0x1p-21f);
+    const bool exact_row = amax_raw >= kInf || !(s >= 0x1p-126f);
+    if (live && lr == 0)
+        scales[row] = s;
+
+    // ---- codes, selection, stores
+    for (int rd = 0; rd < rounds; ++rd) {
+        if (rounds > 1)
+            load(rd);
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int64_t c = rd * kRound + u * kLanes + lr;
+            if (c >= chunks)
+                continue;
+            const uint32_t w[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[2 * i] = bits_to_float(w[i] & 0xffffu, DT);
+                x[2 * i + 1] = bits_to_float(w[i] >> 16, DT);
+            }
+            uint32_t qw[4];                 // four codes per word, element order
+            bool any = exact_row;
+            bool redo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float t[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    t[j] = x[4 * i + j] * y;
+                qw[i] = cvt4(t[0], t[1], t[2], t[3]);
+                redo[i] = qw[i] != cvt4(above(t[0]), above(t[1]), above(t[2]), above(t[3]));
+                any = any || redo[i];
+            }
+            if (any) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (exact_row || redo[i]) {
+                        uint32_t q = 0;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            q |= e4m3_rne_sat(__fdiv_rn(x[4 * i + j], s)) << (8 * j);
+                        qw[i] = q;
+                    }
+                }
+            }
+            if (PRUNE) {
+                uint32_t vw[2], nib = 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t p0, p1;
+                    top2_pair(qw[2 * h], qw[2 * h + 1], p0, p1);
+                    const uint32_t n = p0 | (p1 << 2);           // a metadata nibble per half
+                    nib |= ((n & 0xfu) | ((n >> 12) & 0xf0u)) << (8 * h);
+                    // bytes p of qw[2h] are selector values 0..3, of qw[2h+1] 4..7
+                    vw[h] = __builtin_amdgcn_perm(qw[2 * h + 1], qw[2 * h], p0 | (p1 << 8) | 0x04040000u);
+                }
+                *reinterpret_cast<uint2*>(out + row * (K / 2) + 8 * c) = make_uint2(vw[0], vw[1]);
+                // 16 elements = half a metadata word: lanes 2i and 2i+1 fill word i
+                *reinterpret_cast<uint16_t*>(meta + row * (K / 8) + 2 * c) = (uint16_t)nib;
+            } else {
+                *reinterpret_cast<uint4*>(out + row * K + 16 * c) = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+            }
+        }
+    }
+}
+
+template <sp24_dtype DT, bool PRUNE, int WPR, int CH>
+void launch_shape(int64_t rows, int64_t K, const uint8_t* src, int64_t ld_bytes, uint8_t* out, uint8_t* meta,
+                  float* scales, hipStream_t s) {
+    constexpr int rpb = kWaves / WPR;
+    const dim3 grid((uint32_t)((rows + rpb - 1) / rpb)), block(kThreads);
+    hipLaunchKernelGGL((quantize_rows<DT, PRUNE, WPR, CH>), grid, block, 0, s, src, ld_bytes, rows, K, out, meta,
+                       scales);
+}
+
+// Waves per row and chunks per lane: the whole row in registers up to
+// K = 32768 (one wave per row up to K = 4096, so that many rows are in
+// flight), longer rows in rounds.
+template <sp24_dtype DT, bool PRUNE>
+hipError_t launch_dt(int64_t rows, int64_t K, const uint8_t* src, int64_t ld_bytes, uint8_t* out, uint8_t* meta,
+                     float* scales, hipStream_t s) {
+    const int64_t chunks = K / 16;
+    if (chunks <= 64)
+        launch_shape<DT, PRUNE, 1, 1>(rows, K, src, ld_bytes, out, meta, scales, s);
+    else if (chunks <= 128)
+        launch_shape<DT, PRUNE, 1, 2>(rows, K, src, ld_bytes, out, meta, scales, s);
+    else if (chunks <= 256)
+        launch_shape<DT, PRUNE, 1, 4>(rows, K, src, ld_bytes, out, meta, scales, s);
+    else if (chunks <= 512)
+        launch_shape<DT, PRUNE, 2, 4>(rows, K, src, ld_bytes, out, meta, scales, s);
+    else if (chunks <= 1024)
+        launch_shape<DT, PRUNE, 4, 4>(rows, K, src, ld_bytes, out, meta, scales, s);
+    else
+        launch_shape<DT, PRUNE, 4, kMaxChunks>(rows, K, src, ld_bytes, out, meta, scales, s);
+    return hipGetLastError();
+}
+
+template <bool PRUNE>
+hipError_t launch(sp24_dtype dt, int64_t rows, int64_t K, const void* src, int64_t ld_src, void* out,
+                  uint32_t* meta, float* scales, hipStream_t s) {
+    const int64_t ld_bytes = ld_src * 2;
+    if (dt == SP24_BF16)
+        return launch_dt<SP24_BF16, PRUNE>(rows, K, (const uint8_t*)src, ld_bytes, (uint8_t*)out, (uint8_t*)meta,
+                                           scales, s);
+    return launch_dt<SP24_F16, PRUNE>(rows, K, (const uint8_t*)src, ld_bytes, (uint8_t*)out, (uint8_t*)meta,
+                                      scales, s);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_e4m3(sp24_dtype dt, int64_t rows, int64_t K, const void* src, int64_t ld_src,
+                                void* out, uint32_t* meta, float* scales, hipStream_t s) {
+    return meta ? launch<true>(dt, rows, K, src, ld_src, out, meta, scales, s)
+                : launch<false>(dt, rows, K, src, ld_src, out, nullptr, scales, s);
+}
+
+}  // namespace sp24

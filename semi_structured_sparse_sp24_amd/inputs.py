@@ -20,6 +20,9 @@ Workloads, shaped like the linear layers of the pages' LLMs:
   online    X 4096x4096 bf16 ~N(0, 1) with 1% of entries scaled x20, the
             activation being the operand that is pruned on every call;
             W 4096x4096 bf16 ~N(0, 0.02)
+  online_fp8  the same X (bf16, outliers), quantized to e4m3 per row and
+            pruned on every call by the library; W e4m3 (N, K) in
+            {(4096,4096), (28672,4096)} with per-channel scales; M = 4096
 Seed of tensor t (0 = W, 1 = X, 2 = outlier mask) of shape s in workload c at
 M index j:  10000*c + 100*s + 10*t + j.
 """
@@ -47,6 +50,8 @@ WORKLOADS = {
     "fp8": dict(index=4, dtype=E4M3, out=BF16,
                 shapes=[(5120, 5120), (51200, 5120), (5120, 25600)], ms=[1, 64, 4096]),
     "online": dict(index=5, dtype=BF16, out=BF16, shapes=[(4096, 4096)], ms=[4096]),
+    "online_fp8": dict(index=6, dtype=E4M3, act=BF16, out=BF16, shapes=[(4096, 4096), (28672, 4096)],
+                       ms=[4096]),
 }
 
 
@@ -98,11 +103,12 @@ def activation(workload: str, s: int, j: int, M: int | None = None):
     if M is None:
         M = w["ms"][j]
     t = normal((M, K), 1.0, seed_of(w["index"], s, 1, j))
-    if workload == "online":
+    if workload in ("online", "online_fp8"):
         t = outliers(t, 0.01, 20.0, seed_of(w["index"], s, 2, j))
-    if w["dtype"] == E4M3:
+    act = w.get("act", w["dtype"])
+    if act == E4M3:
         return quantize_e4m3_rows(t)
-    return to_bits(t, w["dtype"]), None
+    return to_bits(t, act), None
 
 
 def integer_operand(shape, seed: int, dt: int, lo: int = -3, hi: int = 3) -> np.ndarray:

@@ -97,6 +97,23 @@ def test_select_tactic_validation():
              ctypes.byref(rec)) == 1
 
 
+def test_quantize_validation_precedes_hip():
+    f, g = sp.lib().sp24_quantize_prune_compress, sp.lib().sp24_quantize_e4m3
+    ok = dict(dt=sp.BF16, rows=4, K=64, src=16, ld=64, out=32, meta=48, sc=64)
+
+    def q(**kw):
+        a = {**ok, **kw}
+        return f(a["dt"], a["rows"], a["K"], a["src"], a["ld"], a["out"], a["meta"], a["sc"], None)
+    assert q(dt=sp.E4M3) == 3 and q(dt=sp.F32) == 3          # the source is 16-bit
+    assert q(rows=-1) == 2 and q(ld=32) == 2
+    assert q(rows=0) == 0 and q(K=0) == 0
+    assert q(src=None) == 1 and q(meta=None) == 1 and q(sc=None) == 1
+    assert q(K=48, ld=48) == 4                                # whole metadata words only
+    assert q(ld=68) == 4 and q(src=24) == 4 and q(sc=66) == 4
+    assert g(sp.F16, 4, 64, 16, 64, None, 64, None) == 1
+    assert g(sp.F16, 4, 48, 16, 48, 32, 64, None) == 4
+
+
 def test_gemm_kernel_names_follow_the_dispatch():
     bf = __import__("torch").bfloat16
     k = sp.gemm_kernel
