@@ -133,7 +133,8 @@ sp24_status sp24_decompress(sp24_dtype dt, int64_t rows, int64_t K,
  *   then the magnitude 2:4 prune and compress of the codes, exactly as
  *   sp24_prune_compress does for SP24_E4M3 input.
  *   src_dt    SP24_F16 or SP24_BF16
- *   rows, K   rows >= 0; K % 32 == 0 (whole metadata words), else SP24_E_ALIGN
+ *   rows, K   0 <= rows <= 2^24 (else SP24_E_SHAPE);
+ *             K % 32 == 0 (whole metadata words), else SP24_E_ALIGN
  *   src       rows x K, row stride ld_src elements (ld_src >= K, ld_src % 8 == 0)
  *   values    out: rows x K/2 e4m3 bytes;  meta  out: rows x K/32 words
  *   scales    out: rows fp32

@@ -147,11 +147,14 @@ SP24_API sp24_status sp24_decompress(sp24_dtype dt, int64_t rows, int64_t K, con
                ? SP24_OK : SP24_E_HIP;
 }
 
+// one 256-lane workgroup per row: the grid stays below 2^32 lanes
+static constexpr int64_t kMaxQuantRows = (int64_t)1 << 24;
+
 static sp24_status quantize_impl(sp24_dtype dt, int64_t rows, int64_t K, const void* src, int64_t ld_src,
                                  void* out, uint32_t* meta, float* scales, bool prune, hipStream_t stream) {
     if (dt != SP24_F16 && dt != SP24_BF16)
         return SP24_E_DTYPE;
-    if (rows < 0 || K < 0 || ld_src < K)
+    if (rows < 0 || K < 0 || ld_src < K || rows > kMaxQuantRows)
         return SP24_E_SHAPE;
     if (rows == 0 || K == 0)
         return SP24_OK;

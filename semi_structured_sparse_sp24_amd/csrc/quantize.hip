@@ -13,12 +13,10 @@
 //   selection is made on them.
 // The plain variant writes all codes (the dense fp8 GEMM's input).
 //
-// A row belongs to one, two or four waves (L = 64, 128 or 256 lanes, the
-// fewest that hold it in registers).  Lane t takes the 16-element chunks
-// t, t + L, ... (two 16-byte loads each) and keeps them: the row is read from
-// memory once, its maximum found with a wave reduction (and LDS words across
-// waves), and the codes formed from the registers.  With one wave per row
-// (K <= 4096) a workgroup holds four rows and no barrier.  Rows longer than
+// A workgroup of 256 lanes per row.  Lane t takes the 16-element chunks
+// t, t + 256, ... (two 16-byte loads each) and keeps them in registers: the
+// row is read from memory once, its maximum found with a wave reduction and
+// four LDS words, and the codes formed from the registers.  Rows longer than
 // 256 * kMaxChunks chunks are taken in rounds and read twice.
 //
 // Codes without the division.  With y = 1/s (correctly rounded, once per row,
@@ -77,7 +75,8 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
 
 // The e4m3 codes of four fp32 values, element order from the low byte.
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // the low-half conversion keeps the old high half, which the second one replaces
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
@@ -117,195 +116,177 @@ __device__ __forceinline__ void top2_pair(uint32_t A, uint32_t B, uint32_t& lo, 
     hi = pmax(pa, pb);
 }
 
+// Maximum over the 64 lanes, in every lane: a prefix maximum within each row
+// of 16 lanes (DPP row shifts, the lanes shifted in from outside the row read
+// 0), the row results carried across rows by the row broadcasts, then lane 63.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));   // row_shr:1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));   // row_shr:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));   // row_shr:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));   // row_shr:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));   // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));   // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Maximum over the WPR waves of one row; every lane of the row gets it.
-// `slot` picks the LDS words, so a second reduction needs no barrier before
-// its writes.
-template <int WPR>
-__device__ __forceinline__ uint32_t row_max_u32(uint32_t v, uint32_t (*red)[kWaves], int slot) {
+// Maximum over the workgroup (one row); every lane gets it.  `red` holds one
+// word per wave and must not be the words the previous reduction read.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v, uint32_t* red) {
     v = wave_max_u32(v);
-    if (WPR == 1)
-        return v;
-    const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0)
-        red[slot][wave] = v;
+        red[threadIdx.x >> 6] = v;
     __syncthreads();
-    const int w0 = wave / WPR * WPR;
-    uint32_t m = red[slot][w0];
-#pragma unroll
-    for (int i = 1; i < WPR; ++i)
-        m = max(m, red[slot][w0 + i]);
-    return m;
+    return max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
-// One row per WPR waves (4 / WPR rows per workgroup), CH chunks per lane and
-// round.  PRUNE: write kept codes + metadata; else write every code.
-template <sp24_dtype DT, bool PRUNE, int WPR, int CH>
+// One row per workgroup, CH chunks per lane and round.  PRUNE: write kept
+// codes + metadata; else write every code.
+template <sp24_dtype DT, bool PRUNE, int CH>
 __global__ void __launch_bounds__(kThreads)
-quantize_rows(const uint8_t* __restrict__ src, int64_t ld_bytes, int64_t rows, int64_t K,
+quantize_rows(const uint8_t* __restrict__ src, int64_t ld_bytes, int64_t K,
               uint8_t* __restrict__ out, uint8_t* __restrict__ meta, float* __restrict__ scales) {
-    constexpr int kLanes = 64 * WPR;                 // lanes per row
-    __shared__ uint32_t red[2][kWaves];
-    const int lr = threadIdx.x % kLanes;
-    const int64_t row = (int64_t)blockIdx.x * (kWaves / WPR) + threadIdx.x / kLanes;
-    // a row of waves past the end: with one wave per row it leaves, else it
-    // still takes part in the workgroup's barriers
-    if (WPR == 1 && row >= rows)
-        return;
-    const bool live = row < rows;
-    const uint8_t* r = src + row * ld_bytes;
-    const int64_t chunks = live ? K / 16 : 0;
-    constexpr int64_t kRound = (int64_t)kLanes * CH;
+    __shared__ uint32_t red[2][kWaves];       // [maximum, NaN-free maximum][wave]
+    const int lr = threadIdx.x;
+    const int64_t chunks = K / 16;
+    constexpr int64_t kRound = (int64_t)kThreads * CH;
     // fewer than kMaxChunks per lane: the launch chose CH so that one round covers the row
-    const int rounds = CH < kMaxChunks ? 1 : (int)((K / 16 + kRound - 1) / kRound);
+    const int rounds = CH < kMaxChunks ? 1 : (int)((chunks + kRound - 1) / kRound);
     constexpr uint32_t kInf = DT == SP24_BF16 ? 0x7f80u : 0x7c00u;   // magnitude bits of +inf
 
-    uint4 a[CH], b[CH];
-    auto load = [&](int rd) {
+    auto load = [&](uint4 (&a)[CH], uint4 (&b)[CH], int64_t row, int rd) {
+        const uint8_t* r = src + row * ld_bytes;
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
-            const int64_t c = rd * kRound + u * kLanes + lr;
+            const int64_t c = rd * kRound + u * kThreads + lr;
             const bool in = c < chunks;
             a[u] = in ? *reinterpret_cast<const uint4*>(r + 32 * c) : make_uint4(0, 0, 0, 0);
             b[u] = in ? *reinterpret_cast<const uint4*>(r + 32 * c + 16) : make_uint4(0, 0, 0, 0);
         }
     };
 
-    // ---- max |x| as magnitude bits (ordered like the values), two halves per word
-    uint32_t mx = 0;
-    for (int rd = 0; rd < rounds; ++rd) {
-        load(rd);
+    uint4 a[CH], b[CH];
+    const int64_t row = blockIdx.x;
+    {
+        const uint8_t* r = src + row * ld_bytes;
+        // ---- max |x| as magnitude bits (ordered like the values), two halves per word
+        uint32_t mx = 0;
+        for (int rd = 0; rd < rounds; ++rd) {
+            load(a, b, row, rd);
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const uint32_t w[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
+            for (int u = 0; u < CH; ++u) {
+                const uint32_t w[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                mx = pmax(mx, w[i] & 0x7fff7fffu);
-        }
-    }
-    const uint32_t amax_raw = row_max_u32<WPR>(max(mx & 0xffffu, mx >> 16), red, 0);
-    uint32_t amax = amax_raw;
-    bool has_nan = amax_raw > kInf;
-    if (WPR > 1)
-        has_nan = __syncthreads_or(has_nan);          // the branch holds a barrier: decide it per workgroup
-    if (has_nan) {
-        // a NaN is in the row: the maximum is taken over the other elements
-        uint32_t m = 0;
-        for (int64_t c = lr; c < chunks; c += kLanes) {
-            const uint4 p = *reinterpret_cast<const uint4*>(r + 32 * c);
-            const uint4 q = *reinterpret_cast<const uint4*>(r + 32 * c + 16);
-            const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t l = w[i] & 0x7fffu, h = (w[i] >> 16) & 0x7fffu;
-                m = max(m, l <= kInf ? l : 0u);
-                m = max(m, h <= kInf ? h : 0u);
+                for (int i = 0; i < 8; ++i)
+                    mx = pmax(mx, w[i] & 0x7fff7fffu);
             }
         }
-        amax = row_max_u32<WPR>(m, red, 1);
-    }
-    const float s = amax ? __fdiv_rn(bits_to_float(amax, DT), 448.0f) : 1.0f;
-    const float y = __fdiv_rn(1.0f, s) * (1.0f - 0x1p-21f);
-    const bool exact_row = amax_raw >= kInf || !(s >= 0x1p-126f);
-    if (live && lr == 0)
-        scales[row] = s;
+        const uint32_t amax_raw = row_max_u32(max(mx & 0xffffu, mx >> 16), red[0]);
+        uint32_t amax = amax_raw;
+        if (amax_raw > kInf) {
+            // a NaN is in the row: the maximum is taken over the other elements
+            uint32_t m = 0;
+            for (int64_t c = lr; c < chunks; c += kThreads) {
+                const uint4 p = *reinterpret_cast<const uint4*>(r + 32 * c);
+                const uint4 q = *reinterpret_cast<const uint4*>(r + 32 * c + 16);
+                const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t l = w[i] & 0x7fffu, h = (w[i] >> 16) & 0x7fffu;
+                    m = max(m, l <= kInf ? l : 0u);
+                    m = max(m, h <= kInf ? h : 0u);
+                }
+            }
+            amax = row_max_u32(m, red[1]);
+        }
+        const float s = amax ? __fdiv_rn(bits_to_float(amax, DT), 448.0f) : 1.0f;
+        const float y = __fdiv_rn(1.0f, s) * (1.0f - 0x1p-21f);
+        const bool exact_row = amax_raw >= kInf || !(s >= 0x1p-126f);
+        if (lr == 0)
+            scales[row] = s;
 
-    // ---- codes, selection, stores
-    for (int rd = 0; rd < rounds; ++rd) {
-        if (rounds > 1)
-            load(rd);
+        // ---- codes, selection, stores
+        for (int rd = 0; rd < rounds; ++rd) {
+            if (rounds > 1)
+                load(a, b, row, rd);
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int64_t c = rd * kRound + u * kLanes + lr;
-            if (c >= chunks)
-                continue;
-            const uint32_t w[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
-            float x[16];
+            for (int u = 0; u < CH; ++u) {
+                const int64_t c = rd * kRound + u * kThreads + lr;
+                if (c >= chunks)
+                    continue;
+                const uint32_t w[8] = {a[u].x, a[u].y, a[u].z, a[u].w, b[u].x, b[u].y, b[u].z, b[u].w};
+                float x[16];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                x[2 * i] = bits_to_float(w[i] & 0xffffu, DT);
-                x[2 * i + 1] = bits_to_float(w[i] >> 16, DT);
-            }
-            uint32_t qw[4];                 // four codes per word, element order
-            bool any = exact_row;
-            bool redo[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float t[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    t[j] = x[4 * i + j] * y;
-                qw[i] = cvt4(t[0], t[1], t[2], t[3]);
-                redo[i] = qw[i] != cvt4(above(t[0]), above(t[1]), above(t[2]), above(t[3]));
-                any = any || redo[i];
-            }
-            if (any) {
+                for (int i = 0; i < 8; ++i) {
+                    x[2 * i] = bits_to_float(w[i] & 0xffffu, DT);
+                    x[2 * i + 1] = bits_to_float(w[i] >> 16, DT);
+                }
+                uint32_t qw[4];                 // four codes per word, element order
+                bool any = exact_row;
+                bool redo[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (exact_row || redo[i]) {
-                        uint32_t q = 0;
+                    float t[4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            q |= e4m3_rne_sat(__fdiv_rn(x[4 * i + j], s)) << (8 * j);
-                        qw[i] = q;
+                    for (int j = 0; j < 4; ++j)
+                        t[j] = x[4 * i + j] * y;
+                    qw[i] = cvt4(t[0], t[1], t[2], t[3]);
+                    redo[i] = qw[i] != cvt4(above(t[0]), above(t[1]), above(t[2]), above(t[3]));
+                    any = any || redo[i];
+                }
+                if (any) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (exact_row || redo[i]) {
+                            uint32_t q = 0;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                q |= e4m3_rne_sat(__fdiv_rn(x[4 * i + j], s)) << (8 * j);
+                            qw[i] = q;
+                        }
                     }
                 }
-            }
-            if (PRUNE) {
-                uint32_t vw[2], nib = 0;
+                if (PRUNE) {
+                    uint32_t vw[2], nib = 0;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    uint32_t p0, p1;
-                    top2_pair(qw[2 * h], qw[2 * h + 1], p0, p1);
-                    const uint32_t n = p0 | (p1 << 2);           // a metadata nibble per half
-                    nib |= ((n & 0xfu) | ((n >> 12) & 0xf0u)) << (8 * h);
-                    // bytes p of qw[2h] are selector values 0..3, of qw[2h+1] 4..7
-                    vw[h] = __builtin_amdgcn_perm(qw[2 * h + 1], qw[2 * h], p0 | (p1 << 8) | 0x04040000u);
+                    for (int h = 0; h < 2; ++h) {
+                        uint32_t p0, p1;
+                        top2_pair(qw[2 * h], qw[2 * h + 1], p0, p1);
+                        const uint32_t n = p0 | (p1 << 2);           // a metadata nibble per half
+                        nib |= ((n & 0xfu) | ((n >> 12) & 0xf0u)) << (8 * h);
+                        // bytes p of qw[2h] are selector values 0..3, of qw[2h+1] 4..7
+                        vw[h] = __builtin_amdgcn_perm(qw[2 * h + 1], qw[2 * h], p0 | (p1 << 8) | 0x04040000u);
+                    }
+                    *reinterpret_cast<uint2*>(out + row * (K / 2) + 8 * c) = make_uint2(vw[0], vw[1]);
+                    // 16 elements = half a metadata word: lanes 2i and 2i+1 fill word i
+                    *reinterpret_cast<uint16_t*>(meta + row * (K / 8) + 2 * c) = (uint16_t)nib;
+                } else {
+                    *reinterpret_cast<uint4*>(out + row * K + 16 * c) = make_uint4(qw[0], qw[1], qw[2], qw[3]);
                 }
-                *reinterpret_cast<uint2*>(out + row * (K / 2) + 8 * c) = make_uint2(vw[0], vw[1]);
-                // 16 elements = half a metadata word: lanes 2i and 2i+1 fill word i
-                *reinterpret_cast<uint16_t*>(meta + row * (K / 8) + 2 * c) = (uint16_t)nib;
-            } else {
-                *reinterpret_cast<uint4*>(out + row * K + 16 * c) = make_uint4(qw[0], qw[1], qw[2], qw[3]);
             }
         }
     }
 }
 
-template <sp24_dtype DT, bool PRUNE, int WPR, int CH>
+template <sp24_dtype DT, bool PRUNE, int CH>
 void launch_shape(int64_t rows, int64_t K, const uint8_t* src, int64_t ld_bytes, uint8_t* out, uint8_t* meta,
                   float* scales, hipStream_t s) {
-    constexpr int rpb = kWaves / WPR;
-    const dim3 grid((uint32_t)((rows + rpb - 1) / rpb)), block(kThreads);
-    hipLaunchKernelGGL((quantize_rows<DT, PRUNE, WPR, CH>), grid, block, 0, s, src, ld_bytes, rows, K, out, meta,
-                       scales);
+    hipLaunchKernelGGL((quantize_rows<DT, PRUNE, CH>), dim3((uint32_t)rows), dim3(kThreads), 0, s, src, ld_bytes,
+                       K, out, meta, scales);
 }
 
-// Waves per row and chunks per lane: the whole row in registers up to
-// K = 32768 (one wave per row up to K = 4096, so that many rows are in
-// flight), longer rows in rounds.
+// Chunks per lane: the whole row in registers up to K = 32768, longer rows in rounds.
 template <sp24_dtype DT, bool PRUNE>
 hipError_t launch_dt(int64_t rows, int64_t K, const uint8_t* src, int64_t ld_bytes, uint8_t* out, uint8_t* meta,
                      float* scales, hipStream_t s) {
     const int64_t chunks = K / 16;
-    if (chunks <= 64)
-        launch_shape<DT, PRUNE, 1, 1>(rows, K, src, ld_bytes, out, meta, scales, s);
-    else if (chunks <= 128)
-        launch_shape<DT, PRUNE, 1, 2>(rows, K, src, ld_bytes, out, meta, scales, s);
-    else if (chunks <= 256)
-        launch_shape<DT, PRUNE, 1, 4>(rows, K, src, ld_bytes, out, meta, scales, s);
-    else if (chunks <= 512)
-        launch_shape<DT, PRUNE, 2, 4>(rows, K, src, ld_bytes, out, meta, scales, s);
-    else if (chunks <= 1024)
-        launch_shape<DT, PRUNE, 4, 4>(rows, K, src, ld_bytes, out, meta, scales, s);
+    if (chunks <= kThreads)
+        launch_shape<DT, PRUNE, 1>(rows, K, src, ld_bytes, out, meta, scales, s);
+    else if (chunks <= 2 * kThreads)
+        launch_shape<DT, PRUNE, 2>(rows, K, src, ld_bytes, out, meta, scales, s);
+    else if (chunks <= 4 * kThreads)
+        launch_shape<DT, PRUNE, 4>(rows, K, src, ld_bytes, out, meta, scales, s);
     else
-        launch_shape<DT, PRUNE, 4, kMaxChunks>(rows, K, src, ld_bytes, out, meta, scales, s);
+        launch_shape<DT, PRUNE, kMaxChunks>(rows, K, src, ld_bytes, out, meta, scales, s);
     return hipGetLastError();
 }
 

@@ -105,7 +105,7 @@ def test_quantize_validation_precedes_hip():
         a = {**ok, **kw}
         return f(a["dt"], a["rows"], a["K"], a["src"], a["ld"], a["out"], a["meta"], a["sc"], None)
     assert q(dt=sp.E4M3) == 3 and q(dt=sp.F32) == 3          # the source is 16-bit
-    assert q(rows=-1) == 2 and q(ld=32) == 2
+    assert q(rows=-1) == 2 and q(ld=32) == 2 and q(rows=(1 << 24) + 1) == 2
     assert q(rows=0) == 0 and q(K=0) == 0
     assert q(src=None) == 1 and q(meta=None) == 1 and q(sc=None) == 1
     assert q(K=48, ld=48) == 4                                # whole metadata words only

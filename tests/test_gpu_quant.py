@@ -56,6 +56,29 @@ def test_plain_matches_oracle_bytewise(dt, rows, K):
     assert np.array_equal(_host(gq), q)
 
 
+# more rows than the workgroups resident at once (with up to 8, 6, 4, 2 of them
+# per compute unit for 1, 2, 4, 8 chunks a lane), so each workgroup walks
+# several rows with the next row's loads in flight; the last shape takes two
+# rounds per row
+LOOP_SHAPES = [(5000, 64), (1600, 4128), (1100, 8224), (600, 16416), (520, 32800)]
+
+
+@pytest.mark.parametrize("rows,K", LOOP_SHAPES)
+def test_rows_walked_by_a_resident_grid(rows, K):
+    say("quant loop", rows, K)
+    bits = _bits(oracle.BF16, rows, K, rows + K, outliers=True)
+    dev = to_dev(bits, oracle.BF16)
+    v, m, s = oracle.quantize_prune_compress(oracle.BF16, bits)
+    gv, gm, gs = sp.quantize_prune_compress(dev)
+    q, s2 = oracle.quantize_e4m3_rows(oracle.BF16, bits)
+    gq, gs2 = sp.quantize_e4m3(dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(gs), s) and np.array_equal(_host(gs2), s2)
+    assert np.array_equal(_host(gv), v)
+    assert np.array_equal(_host(gm).view(np.uint32), m)
+    assert np.array_equal(_host(gq), q)
+
+
 def test_special_rows():
     """All-zero row (scale 1), a row holding one huge outlier, negative zeros,
     subnormal-range quotients, and elements whose fp32 quotient rounds to a
