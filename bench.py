@@ -12,8 +12,11 @@ on (time per launch = chain time / launches).  HBM-bound workloads run "cold": t
 chain cycle through copies of the weights totalling 640 MiB, so every launch
 reads its operands from HBM as successive layers do; compute-bound ones run
 warm on one copy.  After the timed steps the per-shape tactic (sparse iff
-faster) is selected and the CPU oracle is timed on the host cores.  One JSON
-line is printed.
+faster) is selected and the CPU oracle is timed on the host cores.  On the
+bf16 workloads, whose four shapes are the projections of a Llama-3-8B-like
+block, the tactic records also give the layer-level audit manifest of 32
+such blocks per M (its metrics in the line; --manifest-dir writes it whole).
+One JSON line is printed.
 
 Workloads (default: decode, the bf16 Llama-3-8B-like decode layers):
   tiny | decode | prefill | fp8 | online | online_fp8
@@ -33,7 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import semi_structured_sparse_sp24_amd as sp  # noqa: E402
-from semi_structured_sparse_sp24_amd import inputs  # noqa: E402
+from semi_structured_sparse_sp24_amd import audit, inputs  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 SPARSE_PEAK_TFLOPS = {inputs.BF16: 5033.0, inputs.F16: 5033.0, inputs.E4M3: 10066.0}   # 2:4, dense-equivalent
@@ -253,6 +256,31 @@ class Runner:
         return out
 
 
+def layer_audit(workload, w, records, manifest_dir):
+    """The layer-level manifest of a Llama-3-8B-like stack (32 blocks of the four projections
+    whose shapes the bf16 workloads time), one per M, from the tactic records of this run:
+    its metrics go into the bench line, the whole manifest into manifest_dir if given."""
+    shapes = sorted(tuple(x) for x in w["shapes"])
+    if not records or shapes != sorted((N, K) for _, N, K in audit.LLAMA3_8B_BLOCK):
+        return None
+    revision = audit.synthetic_revision(f"{workload}:{w['shapes']}:10000*c + 100*s + 10*t + j")
+    out = {"model": f"Llama-3-8B-like: {audit.LLAMA3_8B_BLOCKS} blocks x (qkv, o, gate_up, down)",
+           "time": "each layer at its selected path's warm median from the tactic record; no time outside "
+                   "these layers (attention, norms) is counted",
+           "per_M": {}}
+    for M in w["ms"]:
+        by_shape = {(N, K): records[(N, K, M)] for _, N, K in audit.LLAMA3_8B_BLOCK}
+        man = audit.block_manifest(by_shape, revision, extra={
+            "workload": {"name": workload, "tokens_per_call": M},
+            "runtime": {"torch": torch.__version__, "hip": torch.version.hip, "lib": sp.version()}})
+        out["per_M"][str(M)] = man["metrics"]
+        if manifest_dir:
+            os.makedirs(manifest_dir, exist_ok=True)
+            with open(os.path.join(manifest_dir, f"manifest_{workload}_M{M}.json"), "w") as f:
+                json.dump(man, f, indent=1)
+    return out
+
+
 def cpu_baseline(workload, budget_s):
     """The oracle as it stands, on the host cores, over a bounded sample of the
     same workload: its GEMMs (fp64 on the decompressed weight) over the
@@ -312,6 +340,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle GEMM time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tactic", action="store_true")
+    ap.add_argument("--manifest-dir", default=None,
+                    help="write the layer-level audit manifest of each M there (bf16 workloads)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -447,6 +477,7 @@ def main():
                            "share": round(v["t"] / all_t, 3)} for n, v in per_kernel.items()}
 
     tactics = []
+    records = {}
     if not args.no_tactic:
         for c in cases:
             for it in c["ms"]:
@@ -466,6 +497,8 @@ def main():
                                            reps=10)
                 tactics.append({"N": N, "K": K, "M": M, "selected": rec["selected"], "ratio": round(rec["ratio"], 3),
                                 "reason": rec["reason"], "kernel": rec["kernel"]})
+                records[(N, K, M)] = rec
+    audit_summary = layer_audit(workload, w, records, args.manifest_dir)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -487,6 +520,7 @@ def main():
         "cpu_baseline": cpu,
         "cases": rows,
         "tactics": tactics,
+        "audit": audit_summary,
         "versions": {"torch": torch.__version__, "hip": torch.version.hip, "lib": sp.version()},
     }
     print(json.dumps(result), flush=True)

@@ -257,6 +257,40 @@ sp24_status sp24_select_tactic(sp24_operand which, sp24_dtype in_dt, sp24_dtype 
 sp24_status sp24_tactic_decide(int eligible, const double *t_sparse, int ns,
                                const double *t_dense, int nd, sp24_tactic *out);
 
+/*
+ * Layer-level audit ("Production 2:4 Structured Sparsity for LLMs", section
+ * "Audit Artifacts and Key Metrics", and step 3 of the playbook, "Run Tactic
+ * Auditing and Profiling"): the counts, ratios and Sparse GPU-Time Coverage
+ * of a model's manifest, aggregated from per-shape tactic records.
+ *   records        n_records tactic records, one per distinct layer shape
+ *   layer_counts   how many of the model's layers share each record (>= 0)
+ *   other_time_us  GPU time of everything outside these layers (attention,
+ *                  norms, ...), >= 0; 0 counts the audited layers alone
+ *   out            host: the metrics
+ * A layer's time is that of its selected path: t_sparse_us + t_compress_us
+ * when it runs sparse (the compress term is 0 for a compressed weight), else
+ * t_dense_us.  Every layer that does not run sparse is a dense fallback,
+ * ineligible ones included.  Ratios with a zero denominator are 0.
+ * A pure host function (no HIP call).  SP24_E_NULL for a missing pointer
+ * (records and layer_counts may be NULL when n_records == 0); SP24_E_SHAPE
+ * for n_records < 0, a negative count, or a negative or non-finite time.
+ */
+typedef struct {
+    int64_t candidate_layers;         /* every audited layer */
+    int64_t eligible_layers;          /* layers whose shape and dtype the sparse path accepts */
+    int64_t sparse_selected_layers;   /* layers that run sparse */
+    int64_t dense_fallback_layers;    /* candidate - sparse selected */
+    double eligibility_ratio;         /* eligible / candidate */
+    double sparse_selection_ratio;    /* sparse selected / eligible */
+    double sparse_gpu_time_us;        /* sum of the time of the layers that run sparse */
+    double total_gpu_time_us;         /* sum of every layer's selected time, + other_time_us */
+    double sparse_gpu_time_coverage;  /* sparse_gpu_time_us / total_gpu_time_us */
+} sp24_audit_metrics;
+
+sp24_status sp24_audit_aggregate(const sp24_tactic *records, const int64_t *layer_counts,
+                                 int64_t n_records, double other_time_us,
+                                 sp24_audit_metrics *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,8 @@ def _load(path=None):
     lib.oracle_quantize_e4m3_rows.argtypes = [i32, i64, i64, vp, i64, vp, vp]
     lib.oracle_gemm.restype = i32
     lib.oracle_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
+    lib.oracle_audit.restype = i32
+    lib.oracle_audit.argtypes = [i64, vp, vp, vp, vp, vp, vp, ctypes.c_double, vp, vp]
     lib.oracle_num_threads.restype = i32
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -229,6 +231,29 @@ def gemm(dt: int, M: int, N: int, K: int, *, x=None, x_vals=None, x_meta=None,
     if rc != 0:
         raise ValueError("oracle_gemm rejected its arguments")
     return R
+
+
+def audit_metrics(records, counts, other_time_us: float = 0.0) -> dict:
+    """Manifest metrics over layer records (dicts with eligible, selected
+    ("sparse" / "dense"), t_sparse_us, t_compress_us, t_dense_us), record i
+    standing for counts[i] layers."""
+    n = len(records)
+    el = np.array([int(bool(r["eligible"])) for r in records] or [0], dtype=np.int32)
+    sel = np.array([int(r["selected"] == "sparse") for r in records] or [0], dtype=np.int32)
+    ts = np.array([float(r["t_sparse_us"]) for r in records] or [0.0])
+    tc = np.array([float(r["t_compress_us"]) for r in records] or [0.0])
+    td = np.array([float(r["t_dense_us"]) for r in records] or [0.0])
+    cnt = np.array(list(counts) or [0], dtype=np.int64)
+    co = np.zeros(4, dtype=np.int64)
+    ro = np.zeros(5)
+    st = _load().oracle_audit(n, _ptr(el), _ptr(sel), _ptr(ts), _ptr(tc), _ptr(td), _ptr(cnt),
+                              float(other_time_us), _ptr(co), _ptr(ro))
+    if st != 0:
+        raise ValueError("oracle_audit rejected its arguments")
+    return {"candidate_layers": int(co[0]), "eligible_layers": int(co[1]), "sparse_selected_layers": int(co[2]),
+            "dense_fallback_layers": int(co[3]), "eligibility_ratio": float(ro[0]),
+            "sparse_selection_ratio": float(ro[1]), "sparse_gpu_time_us": float(ro[2]),
+            "total_gpu_time_us": float(ro[3]), "sparse_gpu_time_coverage": float(ro[4])}
 
 
 def relative_error(Y: np.ndarray, R: np.ndarray) -> float:

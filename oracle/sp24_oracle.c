@@ -22,6 +22,9 @@
  *   decompress  the inverse: kept values back in place, +0.0 elsewhere;
  *   GEMM      Y = X * W^T, computed as the plain dense product of the
  *             decompressed operand with the other operand, in fp64.
+ *   audit     the layer-level manifest metrics of "Production 2:4 Structured
+ *             Sparsity for LLMs" ("Audit Artifacts and Key Metrics"): layer
+ *             counts, selection ratio and Sparse GPU-Time Coverage.
  *
  * Readings of points the pages leave open (each is also listed in the
  * design notes):
@@ -429,6 +432,63 @@ int oracle_gemm(int dt, int64_t M, int64_t N, int64_t K,
         free(wrow);
     }
     free(xs);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Layer-level audit metrics ("Production 2:4 Structured Sparsity for   */
+/* LLMs", section "Audit Artifacts and Key Metrics"; playbook step 3).  */
+/* ------------------------------------------------------------------ */
+
+/*
+ * n distinct layers, layer i standing for count[i] identical model layers.
+ * Walks the model layer by layer:
+ *   every layer is a candidate; eligible[i] marks the eligible ones;
+ *   a layer runs sparse iff it is eligible and its choice is sparse;
+ *   every other layer falls back to dense;
+ *   its GPU time is t_sparse + t_compress when it runs sparse, else t_dense.
+ * Then
+ *   eligibility ratio        = eligible / candidate
+ *   sparse selection ratio   = sparse / eligible
+ *   Sparse GPU-Time Coverage = (time of the sparse layers) /
+ *                              (time of every layer + other_time)
+ * with 0 for a zero denominator.
+ * counts_out: candidate, eligible, sparse, fallback.
+ * ratios_out: eligibility, selection, sparse time, total time, coverage.
+ */
+int oracle_audit(int64_t n, const int *eligible, const int *sparse, const double *t_sparse,
+                 const double *t_compress, const double *t_dense, const int64_t *count,
+                 double other_time, int64_t *counts_out, double *ratios_out)
+{
+    if (n < 0)
+        return OR_E_ARG;
+    int64_t candidate = 0, n_eligible = 0, n_sparse = 0, n_dense = 0;
+    double sparse_time = 0.0, all_time = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        for (int64_t c = 0; c < count[i]; ++c) {
+            candidate += 1;
+            if (eligible[i])
+                n_eligible += 1;
+            if (eligible[i] && sparse[i]) {
+                n_sparse += 1;
+                sparse_time += t_sparse[i] + t_compress[i];
+                all_time += t_sparse[i] + t_compress[i];
+            } else {
+                n_dense += 1;
+                all_time += t_dense[i];
+            }
+        }
+    }
+    all_time += other_time;
+    counts_out[0] = candidate;
+    counts_out[1] = n_eligible;
+    counts_out[2] = n_sparse;
+    counts_out[3] = n_dense;
+    ratios_out[0] = candidate > 0 ? (double)n_eligible / (double)candidate : 0.0;
+    ratios_out[1] = n_eligible > 0 ? (double)n_sparse / (double)n_eligible : 0.0;
+    ratios_out[2] = sparse_time;
+    ratios_out[3] = all_time;
+    ratios_out[4] = all_time > 0.0 ? sparse_time / all_time : 0.0;
     return OR_OK;
 }
 

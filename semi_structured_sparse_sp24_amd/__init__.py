@@ -15,6 +15,7 @@ PyTorch fallback: if the library is missing, every call raises.
   gemm_kernel(...)             -> name of the kernel a GEMM call would launch (host only)
   quantize_prune_compress(x)   -> (values e4m3, meta, scales): fused online fp8 path
   quantize_e4m3(x)             -> (codes e4m3, scales): the dense side's quantization
+  audit_aggregate(...)         -> layer counts, ratios and Sparse GPU-Time Coverage (host only)
 """
 from __future__ import annotations
 
@@ -48,6 +49,17 @@ class Tactic(ctypes.Structure):
                 "reason": self.reason.decode(), "kernel": self.kernel.decode()}
 
 
+class AuditMetrics(ctypes.Structure):
+    _fields_ = [("candidate_layers", ctypes.c_int64), ("eligible_layers", ctypes.c_int64),
+                ("sparse_selected_layers", ctypes.c_int64), ("dense_fallback_layers", ctypes.c_int64),
+                ("eligibility_ratio", ctypes.c_double), ("sparse_selection_ratio", ctypes.c_double),
+                ("sparse_gpu_time_us", ctypes.c_double), ("total_gpu_time_us", ctypes.c_double),
+                ("sparse_gpu_time_coverage", ctypes.c_double)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 SIGNATURES = {
     "sp24_status_str": (ctypes.c_char_p, [_i32]),
     "sp24_version": (ctypes.c_char_p, []),
@@ -61,6 +73,8 @@ SIGNATURES = {
     "sp24_tactic_decide": (_i32, [_i32, ctypes.POINTER(_dbl), _i32, ctypes.POINTER(_dbl), _i32,
                                   ctypes.POINTER(Tactic)]),
     "sp24_gemm_kernel": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i64, _i64, _i64]),
+    "sp24_audit_aggregate": (_i32, [ctypes.POINTER(Tactic), ctypes.POINTER(_i64), _i64, _dbl,
+                                    ctypes.POINTER(AuditMetrics)]),
     "sp24_quantize_prune_compress": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp]),
     "sp24_quantize_e4m3": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
 }
@@ -217,6 +231,31 @@ def tactic_decide(eligible: bool, t_sparse, t_dense) -> dict:
     st = lib().sp24_tactic_decide(int(eligible), ts, len(t_sparse), td, len(t_dense), ctypes.byref(rec))
     _check("sp24_tactic_decide", st)
     return rec.as_dict()
+
+
+def tactic_record(rec: dict) -> Tactic:
+    """A record dict (as select_tactic returns) back in the C layout."""
+    t = Tactic()
+    t.eligible = int(bool(rec["eligible"]))
+    t.selected = 1 if rec["selected"] == "sparse" else 0
+    t.t_sparse_us, t.t_compress_us = float(rec["t_sparse_us"]), float(rec["t_compress_us"])
+    t.t_dense_us, t.ratio = float(rec["t_dense_us"]), float(rec["ratio"])
+    t.reason = rec["reason"].encode()[:95]
+    t.kernel = rec["kernel"].encode()[:63]
+    return t
+
+
+def audit_aggregate(records, layer_counts, other_time_us: float = 0.0) -> dict:
+    """Manifest metrics over per-shape tactic records (dicts), each shared by layer_counts[i] layers."""
+    n = len(records)
+    if len(layer_counts) != n:
+        raise ValueError("one layer count per record")
+    arr = (Tactic * max(1, n))(*[tactic_record(r) for r in records])
+    cnt = (_i64 * max(1, n))(*[int(c) for c in layer_counts])
+    out = AuditMetrics()
+    _check("sp24_audit_aggregate", lib().sp24_audit_aggregate(arr, cnt, n, float(other_time_us),
+                                                             ctypes.byref(out)))
+    return out.as_dict()
 
 
 def gemm_kernel(sparse: bool, which: int, in_dtype, out_dtype, M: int, N: int, K: int):

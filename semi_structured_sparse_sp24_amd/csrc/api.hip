@@ -2,6 +2,7 @@
 // validation (on the host, before any HIP call), dispatch to the kernels,
 // and the sparse-versus-dense tactic selection.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <vector>
@@ -309,6 +310,44 @@ SP24_API sp24_status sp24_tactic_decide(int eligible, const double* t_sparse, in
         snprintf(out->reason, sizeof(out->reason), "Tie: dense kept (sparse not faster)");
     else
         snprintf(out->reason, sizeof(out->reason), "Dense kernel %.2fx faster", ts / out->t_dense_us);
+    return SP24_OK;
+}
+
+SP24_API sp24_status sp24_audit_aggregate(const sp24_tactic* records, const int64_t* layer_counts,
+                                          int64_t n_records, double other_time_us, sp24_audit_metrics* out) {
+    if (!out)
+        return SP24_E_NULL;
+    if (n_records < 0 || !std::isfinite(other_time_us) || other_time_us < 0.0)
+        return SP24_E_SHAPE;
+    if (n_records > 0 && (!records || !layer_counts))
+        return SP24_E_NULL;
+    sp24_audit_metrics m{};
+    double total = 0.0;
+    for (int64_t i = 0; i < n_records; ++i) {
+        const sp24_tactic& r = records[i];
+        const int64_t c = layer_counts[i];
+        const double ts = r.t_sparse_us + r.t_compress_us;
+        if (c < 0 || !std::isfinite(ts) || !std::isfinite(r.t_dense_us) || r.t_sparse_us < 0.0 ||
+            r.t_compress_us < 0.0 || r.t_dense_us < 0.0)
+            return SP24_E_SHAPE;
+        m.candidate_layers += c;
+        if (r.eligible)
+            m.eligible_layers += c;
+        if (r.eligible && r.selected) {
+            m.sparse_selected_layers += c;
+            m.sparse_gpu_time_us += (double)c * ts;
+            total += (double)c * ts;
+        } else {
+            total += (double)c * r.t_dense_us;
+        }
+    }
+    m.dense_fallback_layers = m.candidate_layers - m.sparse_selected_layers;
+    m.total_gpu_time_us = total + other_time_us;
+    m.eligibility_ratio = m.candidate_layers ? (double)m.eligible_layers / (double)m.candidate_layers : 0.0;
+    m.sparse_selection_ratio =
+        m.eligible_layers ? (double)m.sparse_selected_layers / (double)m.eligible_layers : 0.0;
+    m.sparse_gpu_time_coverage = m.total_gpu_time_us > 0.0 ? m.sparse_gpu_time_us / m.total_gpu_time_us : 0.0;
+    *out = m;
     return SP24_OK;
 }
 

@@ -22,7 +22,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("sp24_prune_compress", "sp24_decompress", "sp24_gemm", "dense_gemm",
-                     "sp24_select_tactic", "sp24_tactic_decide", "sp24_status_str"):
+                     "sp24_select_tactic", "sp24_tactic_decide", "sp24_status_str", "sp24_audit_aggregate"):
         assert required in names
 
 
@@ -176,3 +176,66 @@ def test_decide_rejects_missing_timings():
         sp.tactic_decide(True, [], [1.0])
     with pytest.raises(sp.Sp24Error):
         sp.tactic_decide(True, [1.0], [])
+
+
+def _audit_rec(eligible, selected, ts, tc, td):
+    return dict(eligible=eligible, selected=selected, t_sparse_us=ts, t_compress_us=tc, t_dense_us=td,
+                ratio=1.0, reason="r", kernel="k")
+
+
+def test_audit_aggregate_matches_the_oracle():
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(17)
+    for trial in range(40):
+        n = int(rng.integers(0, 9))
+        recs = []
+        for _ in range(n):
+            el = bool(rng.integers(0, 4))
+            recs.append(_audit_rec(el, "sparse" if rng.integers(0, 2) else "dense", float(rng.uniform(0, 200)),
+                                   float(rng.uniform(0, 20) * rng.integers(0, 2)), float(rng.uniform(0, 200))))
+        counts = [int(c) for c in rng.integers(0, 64, n)]
+        other = float(rng.uniform(0, 100) * rng.integers(0, 2))
+        got = sp.audit_aggregate(recs, counts, other)
+        want = oracle.audit_metrics(recs, counts, other)
+        for k in ("candidate_layers", "eligible_layers", "sparse_selected_layers", "dense_fallback_layers"):
+            assert got[k] == want[k], (trial, k)
+        for k in ("eligibility_ratio", "sparse_selection_ratio", "sparse_gpu_time_us", "total_gpu_time_us",
+                  "sparse_gpu_time_coverage"):
+            assert abs(got[k] - want[k]) <= 1e-12 * max(1.0, abs(want[k])), (trial, k)
+
+
+def test_audit_aggregate_validation():
+    lib = sp.lib()
+    out = sp.AuditMetrics()
+    recs = (sp.Tactic * 1)(sp.tactic_record(_audit_rec(True, "sparse", 1.0, 0.0, 2.0)))
+    one = (ctypes.c_int64 * 1)(3)
+    assert lib.sp24_audit_aggregate(recs, one, 1, 0.0, None) == 1
+    assert lib.sp24_audit_aggregate(None, one, 1, 0.0, ctypes.byref(out)) == 1
+    assert lib.sp24_audit_aggregate(recs, None, 1, 0.0, ctypes.byref(out)) == 1
+    assert lib.sp24_audit_aggregate(None, None, 0, 0.0, ctypes.byref(out)) == 0 and out.candidate_layers == 0
+    assert lib.sp24_audit_aggregate(recs, one, -1, 0.0, ctypes.byref(out)) == 2
+    assert lib.sp24_audit_aggregate(recs, one, 1, -1.0, ctypes.byref(out)) == 2
+    assert lib.sp24_audit_aggregate(recs, one, 1, float("nan"), ctypes.byref(out)) == 2
+    neg = (ctypes.c_int64 * 1)(-1)
+    assert lib.sp24_audit_aggregate(recs, neg, 1, 0.0, ctypes.byref(out)) == 2
+    bad = (sp.Tactic * 1)(sp.tactic_record(_audit_rec(True, "sparse", float("inf"), 0.0, 2.0)))
+    assert lib.sp24_audit_aggregate(bad, one, 1, 0.0, ctypes.byref(out)) == 2
+    assert lib.sp24_audit_aggregate(recs, one, 1, 0.0, ctypes.byref(out)) == 0
+    assert (out.candidate_layers, out.sparse_selected_layers, out.sparse_gpu_time_coverage) == (3, 3, 1.0)
+
+
+def test_block_manifest_layout():
+    from semi_structured_sparse_sp24_amd import audit
+    recs = {}
+    for i, (_, N, K) in enumerate(audit.LLAMA3_8B_BLOCK):
+        recs[(N, K)] = _audit_rec(i != 1, "sparse" if i in (0, 2) else "dense", 10.0, 0.0, 12.0)
+    recs[(4096, 4096)]["reason"] = "Alignment failure"
+    m = audit.block_manifest(recs, "rev")
+    assert m["sparsity_pattern"] == "2:4" and m["model_revision"] == "rev"
+    assert len(m["layers"]) == 4 * audit.LLAMA3_8B_BLOCKS == m["metrics"]["candidate_layers"]
+    assert m["metrics"]["sparse_selected_layers"] == 64 and m["metrics"]["eligible_layers"] == 96
+    assert m["layers"]["model.layers.31.self_attn.o_proj"] == {"eligible": False, "selected": "dense",
+                                                              "reason": "Alignment failure"}
+    assert m["layers"]["model.layers.0.mlp.gate_up_proj"] == {"eligible": True, "selected": "sparse"}
+    assert "reason" in m["layers"]["model.layers.5.mlp.down_proj"]

@@ -7,6 +7,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_audit as audit
 from tests import test_oracle_codecs as codecs
 from tests import test_oracle_gemm as gemm
 from tests import test_oracle_prune as prune
@@ -34,6 +35,10 @@ MUTANTS = [
     ("quant-scale-off", "amax / 448.0f", "amax / 447.0f"),
     ("quant-scale-fp64", "float t = v / sc;", "double t = (double)v / (double)sc;"),
     ("quant-absmax-signed", "float a = fabsf(v);", "float a = v;"),
+    ("audit-coverage-drops-compress", "sparse_time += t_sparse[i] + t_compress[i];", "sparse_time += t_sparse[i];"),
+    ("audit-fallback-skips-ineligible", "n_dense += 1;", "n_dense += eligible[i] ? 1 : 0;"),
+    ("audit-selection-over-candidates", "(double)n_sparse / (double)n_eligible", "(double)n_sparse / (double)candidate"),
+    ("audit-ignores-eligibility", "if (eligible[i] && sparse[i]) {", "if (sparse[i]) {"),
 ]
 
 PINS = [
@@ -53,6 +58,10 @@ PINS = [
     lambda: quant.test_quantize_exact_round_trip(oracle.BF16),
     lambda: quant.test_quantize_row_maximum_and_error_bound(oracle.BF16),
     quant.test_quantize_decides_codes_in_fp32,
+    audit.test_page_example_counts_and_selection_ratio,
+    audit.test_coverage_worked_by_hand,
+    audit.test_invariants,
+    audit.test_extremes,
 ]
 
 
