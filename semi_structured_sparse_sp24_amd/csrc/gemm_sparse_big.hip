@@ -7,13 +7,16 @@
 //
 // Design (shown for the 256 x 256 tile; smaller tiles for outputs that would
 // not fill the chip follow the same plan with fewer rows):
-//   - tile 256 (A rows) x 256 (B rows); 8 waves in a 4 x 2 grid (two per
-//     SIMD), each owning 64 x 128 = 4 x 8 fragments of v_smfmac_f32_16x16x64
+//   - tile 256 (A rows) x 256 (B rows); 8 waves in a 2 x 4 grid (two per
+//     SIMD), each owning 128 x 64 = 8 x 4 fragments of v_smfmac_f32_16x16x64
 //     (16-bit) or v_smfmac_f32_16x16x128 (fp8), accumulated in 128 registers
-//     per lane.  (One wave per SIMD with 128 x 128 each needs 256 accumulator
-//     registers plus operands, and the compiler then shuffles accumulators
-//     between register files inside the loop; two waves per SIMD also hide
-//     each other's LDS latency.)
+//     per lane.  Every wave reads its A and B rows from LDS each step, so the
+//     grid sets the LDS read traffic: 2 x 4 reads the half-width A four
+//     times and B twice, 128 KiB per step, where 4 x 2 reads 160 KiB (and
+//     runs 4% slower).  (One wave per SIMD with 128 x 128 each needs 256
+//     accumulator registers plus operands, and the compiler then shuffles
+//     accumulators between register files inside the loop; two waves per
+//     SIMD also hide each other's LDS latency.)
 //   - K advances one instruction step per stage: A 256 rows x 64 B and B 256
 //     rows x 128 B; metadata comes in blocks of 16 B per row (two 16-bit
 //     steps, or one fp8 step); three stages and three metadata blocks live in
@@ -45,7 +48,7 @@ struct Tile {
     static constexpr int B_STAGE = BB * 128;   // bytes of dense B per stage
     static constexpr int M_BLOCK = BA * 16;    // bytes of one metadata block
 };
-using T256x256 = Tile<256, 256, 4, 2, 1>;
+using T256x256 = Tile<256, 256, 2, 4, 1>;
 using T256x128 = Tile<256, 128, 4, 2, 1>;
 using T128x128 = Tile<128, 128, 2, 4, 2>;
 using T256x64 = Tile<256, 64, 4, 2, 1>;
