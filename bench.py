@@ -19,7 +19,7 @@ such blocks per M (its metrics in the line; --manifest-dir writes it whole).
 One JSON line is printed.
 
 Workloads (default: decode, the bf16 Llama-3-8B-like decode layers):
-  tiny | decode | prefill | fp8 | online | online_fp8
+  tiny | decode | prefill | fp8 | online | online_fp8 | hybrid
 """
 from __future__ import annotations
 
@@ -63,6 +63,11 @@ def dense_gemm_bytes(M, N, K, eb, out_eb, scales):
     return (M + N) * K * eb + M * N * out_eb + (4 * (M + N) if scales else 0)
 
 
+def hybrid_gemm_bytes(M, NS, ND, K, eb, out_eb):
+    """Compressed rows (values + meta) + dense rows + X + the whole output."""
+    return NS * K * eb // 2 + NS * K // 8 + ND * K * eb + M * K * eb + M * (NS + ND) * out_eb
+
+
 def compress_bytes(R, K, eb):
     return R * K * eb + R * K * eb // 2 + R * K // 8
 
@@ -96,6 +101,7 @@ def traffic_per_launch(kernel, workload):
 # on one copy.
 COLD_BYTES = 640 << 20
 ONLINE = ("online", "online_fp8")   # the activation is the compressed operand, compressed every call
+HYBRID = "hybrid"                   # weight rows split: 2:4 rows and dense rows in one launch
 MAX_COPIES = 64
 # The shortest chain of a workload runs for about this long, so that the fixed cost of starting a
 # graph (~20 us) stays a small part of the bracketed time.  Every GEMM chain of a workload has the
@@ -132,13 +138,22 @@ def build_cases(workload, cold):
         wb, sw = inputs.weight(workload, s)
         W0 = dev(wb, dt)
         shape = {"s": s, "N": N, "K": K, "sw": None if sw is None else torch.from_numpy(sw).cuda(), "ms": []}
-        nc = 1 if workload in ONLINE else n_copies(N * K * eb // 2 + N * K // 8, cold)
+        NS = N
+        if workload == HYBRID:
+            # the first NS rows go 2:4, the rest stay dense; the dense baseline runs the same weight
+            # (the pruned rows and the dense rows) through the dense GEMM
+            NS, ND = inputs.hybrid_split(N)
+            shape.update(NS=NS, ND=ND, Wd=W0[NS:].contiguous())
+            W0 = W0[:NS].contiguous()
+        nc = 1 if workload in ONLINE else n_copies(NS * K * eb // 2 + NS * K // 8, cold)
         copies = []
         for i in range(nc):
             W = W0 if i == 0 else W0.clone()
             v, m = sp.prune_compress(W)
             copies.append({"W": W, "v": v, "m": m, "Wp": sp.decompress(v, m, K)})
         shape["copies"] = copies
+        if workload == HYBRID:
+            shape["Wfull"] = torch.cat([copies[0]["Wp"], shape["Wd"]]).contiguous()
         for j, M in enumerate(w["ms"]):
             xb, sx = inputs.activation(workload, s, j)
             X = dev(xb, w.get("act", dt))
@@ -148,6 +163,9 @@ def build_cases(workload, cold):
             if workload in ONLINE:
                 item["xv"] = torch.empty((M, K // 2), dtype=TORCH[dt], device="cuda")
                 item["xm"] = torch.empty((M, (K + 31) // 32), dtype=torch.int32, device="cuda")
+            if workload == HYBRID:
+                item["Ys"] = torch.empty((M, shape["NS"]), dtype=ytype, device="cuda")
+                item["Ydd"] = torch.empty((M, shape["ND"]), dtype=ytype, device="cuda")
             if workload == "online_fp8":
                 # each side quantizes the bf16 activation itself: fused with the prune for the
                 # sparse side, plain for the dense side
@@ -195,6 +213,20 @@ def chains(workload, cases):
                 out.append((("dense",) + key, Lg,
                             lambda i, it=it, W=W, sw=sw: sp.dense_gemm(it["xq"], W, scale_x=it["xqs"], scale_w=sw,
                                                                        out=it["Yd"])))
+                continue
+            if workload == HYBRID:
+                # one launch for both regions; against the dense GEMM on the whole weight, and against
+                # the same split as two launches (sparse GEMM on the 2:4 rows, dense GEMM on the rest)
+                NS, ND, Wd, Wf = c["NS"], c["ND"], c["Wd"], c["Wfull"]
+                out.append((("sparse",) + key, Lg,
+                            lambda i, it=it, pick=pick, Wd=Wd, NS=NS, ND=ND:
+                            sp.hybrid_gemm(pick(i)["v"], pick(i)["m"], Wd, it["X"], NS, ND, out=it["Y"])))
+                out.append((("dense",) + key, Lg, lambda i, it=it, Wf=Wf: sp.dense_gemm(it["X"], Wf, out=it["Yd"])))
+
+                def split(i, it=it, pick=pick, Wd=Wd, M=M, NS=NS, K=K):
+                    sp.sp24_gemm(sp.SPARSE_W, pick(i)["v"], pick(i)["m"], it["X"], M, NS, K, out=it["Ys"])
+                    sp.dense_gemm(it["X"], Wd, out=it["Ydd"])
+                out.append((("split",) + key, Lg, split))
                 continue
             if workload == "online":
                 # the activation is the sparse operand: prune+compress it on every call
@@ -294,7 +326,10 @@ def cpu_baseline(workload, budget_s):
     for s, (N, K) in enumerate(w["shapes"]):
         wb, sw = inputs.weight(workload, s)
         wv = wm = None
-        if workload not in ONLINE:
+        if workload == HYBRID:
+            NS, _ = inputs.hybrid_split(N)
+            wv, wm = oracle.prune_compress(dt, wb[:NS])
+        elif workload not in ONLINE:
             wv, wm = oracle.prune_compress(dt, wb)
         for j, M in enumerate(w["ms"]):
             xb, sx = inputs.activation(workload, s, j)
@@ -315,6 +350,9 @@ def cpu_baseline(workload, budget_s):
             t0 = time.perf_counter()
             if workload in ONLINE:
                 oracle.gemm(dt, M, N, K, x_vals=xv, x_meta=xm, w=wb, scale_x=sx, scale_w=sw, mrows=mrows)
+            elif workload == HYBRID:
+                NS, ND = inputs.hybrid_split(N)
+                oracle.hybrid_gemm(dt, rows, NS, ND, K, x=xb[mrows], ws_vals=wv, ws_meta=wm, wd=wb[NS:])
             else:
                 oracle.gemm(dt, M, N, K, x=xb, w_vals=wv, w_meta=wm, scale_x=sx, scale_w=sw, mrows=mrows)
             secs += time.perf_counter() - t0
@@ -399,7 +437,10 @@ def main():
             ts = times[("sparse",) + key]
             td = times[("dense",) + key]
             sparse_rows = M if workload in ONLINE else N
-            sb = sparse_gemm_bytes(M, N, K, eb, out_eb, sparse_rows, scales)
+            if workload == HYBRID:
+                sb = hybrid_gemm_bytes(M, c["NS"], c["ND"], K, eb, out_eb)
+            else:
+                sb = sparse_gemm_bytes(M, N, K, eb, out_eb, sparse_rows, scales)
             db = dense_gemm_bytes(M, N, K, eb, out_eb, scales)
             fl = 2.0 * M * N * K
             tsm, tdm = float(np.median(ts)), float(np.median(td))
@@ -409,6 +450,10 @@ def main():
                    "sparse_GBps": round(sb / tsm / 1e3, 1), "dense_GBps": round(db / tdm / 1e3, 1),
                    "sparse_hbm_frac": round(sb / tsm / 1e3 / HBM_PEAK_GBPS, 3),
                    "sparse_mfma_frac": round(fl / tsm / 1e6 / SPARSE_PEAK_TFLOPS[dt], 3)}
+            if workload == HYBRID:
+                tsp = float(np.median(times[("split",) + key]))
+                row.update(N_s=c["NS"], N_d=c["ND"], t_two_launch_us=round(tsp, 2),
+                           speedup_vs_two_launch=round(tsp / tsm, 3))
             if workload in ONLINE:
                 tc = float(np.median(times[("compress",) + key]))
                 tp = float(np.median(times[("prep",) + key])) if workload == "online_fp8" else 0.0
@@ -429,7 +474,7 @@ def main():
         if workload not in ONLINE:
             tcs = times[("compress", c["s"])]
             tot["compress_t"] += sum(tcs)
-            tot["compress_bytes"] += compress_bytes(N, K, eb) * len(tcs)
+            tot["compress_bytes"] += compress_bytes(c.get("NS", N), K, eb) * len(tcs)
 
     value = tot["flops"] / tot["sparse_t"] / 1e6                    # TFLOP/s (dense-equivalent)
     speedup = tot["dense_t"] / tot["sparse_t"]
@@ -444,15 +489,25 @@ def main():
         for it in c["ms"]:
             M, N, K = it["M"], c["N"], c["K"]
             which = sp.SPARSE_X if workload in ONLINE else sp.SPARSE_W
-            name = sp.gemm_kernel(True, which, TORCH[dt], it["Y"].dtype, M, N, K)
+            if workload == HYBRID:
+                name = sp.hybrid_kernel(TORCH[dt], it["Y"].dtype, M, c["NS"], c["ND"], K)
+            else:
+                name = sp.gemm_kernel(True, which, TORCH[dt], it["Y"].dtype, M, N, K)
             key = ("sparse", c["s"], it["j"])
             ts, L = times[key], runner.length[key]       # per-launch means of each step; chain length
             sparse_rows = M if workload in ONLINE else N
-            k = per_kernel.setdefault(name, {"t": 0.0, "n": 0, "bytes": 0.0, "flops": 0.0})
+            k = per_kernel.setdefault(name, {"t": 0.0, "n": 0, "bytes": 0.0, "flops": 0.0, "t_peak": 0.0})
             # weighted by launches, as a profiler's per-kernel average is
             k["t"] += sum(ts) * L
             k["n"] += len(ts) * L
-            k["bytes"] += sparse_gemm_bytes(M, N, K, eb, out_eb, sparse_rows, scales) * len(ts) * L
+            if workload == HYBRID:
+                k["bytes"] += hybrid_gemm_bytes(M, c["NS"], c["ND"], K, eb, out_eb) * len(ts) * L
+                # time at peak: the 2:4 rows at the sparse rate, the dense rows at the dense rate
+                k["t_peak"] += (2.0 * M * K * (c["NS"] / SPARSE_PEAK_TFLOPS[dt] + c["ND"] / DENSE_PEAK_TFLOPS[dt])
+                                / 1e6) * len(ts) * L
+            else:
+                k["bytes"] += sparse_gemm_bytes(M, N, K, eb, out_eb, sparse_rows, scales) * len(ts) * L
+                k["t_peak"] += 2.0 * M * N * K / SPARSE_PEAK_TFLOPS[dt] / 1e6 * len(ts) * L
             k["flops"] += 2.0 * M * N * K * len(ts) * L
     kname = max(per_kernel, key=lambda n: per_kernel[n]["t"])
     k = per_kernel[kname]
@@ -466,7 +521,9 @@ def main():
                 "kernel": kname, "launches": k["n"], "bytes_per_launch": round(k["bytes"] / k["n"]),
                 "avg_launch_us": round(avg_us, 3)}
     else:
-        peak = SPARSE_PEAK_TFLOPS[dt]
+        # the kernel's own peak in dense-equivalent flops (for the hybrid, the rate at which its mix of
+        # 2:4 and dense rows would run with every instruction at peak)
+        peak = round(k["flops"] / k["t_peak"] / 1e6, 1)
         achieved = k["flops"] / k["t"] / 1e6
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic_per_launch(kname, workload),
@@ -478,7 +535,7 @@ def main():
 
     tactics = []
     records = {}
-    if not args.no_tactic:
+    if not args.no_tactic and workload != HYBRID:
         for c in cases:
             for it in c["ms"]:
                 M, N, K = it["M"], c["N"], c["K"]

@@ -195,6 +195,42 @@ sp24_status dense_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N
                        void *Y, hipStream_t stream);
 
 /*
+ * Hybrid sparse + dense GEMM in one launch ("Production 2:4 Structured
+ * Sparsity for LLMs", section "Dense Fallback and Hybrid Sparsity Design":
+ * dense regions kept next to 2:4 regions of one weight, as SpenseGPT does).
+ * The weight's output channels are split by row: the first N_s rows are
+ * 2:4-compressed, the next N_d rows stay dense, and the outputs are disjoint:
+ *   Y[m][n]       = sum_k X[m][k] * Ws[n][k]          n <  N_s
+ *   Y[m][N_s + n] = sum_k X[m][k] * Wd[n][k]          n <  N_d
+ * (times scale_x[m] * scale_w[column] for fp8).  The caller chooses which
+ * rows go where and orders them so (any row permutation of W permutes the
+ * columns of Y alike).  One kernel runs both regions: its dense tiles feed
+ * the same sparse instruction twice per group of four, once with positions
+ * (0, 1) and once with (2, 3), so both regions share the pipeline and the
+ * epilogue and no region waits for the other.
+ *   in_dt, out_dt  as sp24_gemm
+ *   M, N_s, N_d, K M, N_s, N_d >= 0; K % 64 (16-bit) or K % 128 (fp8), else
+ *                  SP24_E_ALIGN; N_s % 8 == 0 (the dense outputs start on a
+ *                  16-byte boundary), else SP24_E_ALIGN
+ *   values, meta   Ws compressed: N_s x K/2 values, N_s x K/32 words
+ *   W_d            N_d x K dense, row-major
+ *   X              M x K dense, row-major
+ *   scale_x        M floats or NULL;  scale_w  N_s + N_d floats or NULL
+ *   Y              M x (N_s + N_d) of out_dt, row-major
+ * Same sizes limits, alignment and errors as sp24_gemm; values/meta may be
+ * NULL when N_s == 0 and W_d when N_d == 0.
+ */
+sp24_status sp24_hybrid_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N_s, int64_t N_d,
+                             int64_t K, const void *values, const uint32_t *meta, const void *W_d,
+                             const void *X, const float *scale_x, const float *scale_w, void *Y,
+                             hipStream_t stream);
+
+/* The name of the kernel sp24_hybrid_gemm launches for this shape, as
+ * sp24_gemm_kernel does for the plain GEMMs (host only; NULL if rejected). */
+const char *sp24_hybrid_kernel(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N_s,
+                               int64_t N_d, int64_t K);
+
+/*
  * The name of the kernel that sp24_gemm (sparse != 0) or dense_gemm
  * (sparse == 0) launches for this shape and dtype, without launching
  * anything: a pure host function, no HIP call.  The same names appear in

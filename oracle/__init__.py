@@ -233,6 +233,22 @@ def gemm(dt: int, M: int, N: int, K: int, *, x=None, x_vals=None, x_meta=None,
     return R
 
 
+def hybrid_gemm(dt: int, M: int, NS: int, ND: int, K: int, *, x, ws_vals=None, ws_meta=None, wd=None,
+                scale_x=None, scale_w=None):
+    """The row-split hybrid ("Production 2:4 Structured Sparsity for LLMs",
+    "Dense Fallback and Hybrid Sparsity Design"): R = X [Ws | Wd]^T, the first
+    NS output columns from the 2:4 rows (decompressed), the next ND from the
+    dense rows; each block is the plain product of gemm()."""
+    R = np.zeros((M, NS + ND), dtype=np.float64)
+    sw = None if scale_w is None else np.asarray(scale_w, dtype=np.float32)
+    if NS > 0:
+        R[:, :NS] = gemm(dt, M, NS, K, x=x, w_vals=ws_vals, w_meta=ws_meta, scale_x=scale_x,
+                         scale_w=None if sw is None else sw[:NS])
+    if ND > 0:
+        R[:, NS:] = gemm(dt, M, ND, K, x=x, w=wd, scale_x=scale_x, scale_w=None if sw is None else sw[NS:])
+    return R
+
+
 def audit_metrics(records, counts, other_time_us: float = 0.0) -> dict:
     """Manifest metrics over layer records (dicts with eligible, selected
     ("sparse" / "dense"), t_sparse_us, t_compress_us, t_dense_us), record i

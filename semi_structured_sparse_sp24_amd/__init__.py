@@ -15,6 +15,7 @@ PyTorch fallback: if the library is missing, every call raises.
   gemm_kernel(...)             -> name of the kernel a GEMM call would launch (host only)
   quantize_prune_compress(x)   -> (values e4m3, meta, scales): fused online fp8 path
   quantize_e4m3(x)             -> (codes e4m3, scales): the dense side's quantization
+  hybrid_gemm(...)             -> Y = X [Ws | Wd]^T, Ws compressed and Wd dense rows, one launch
   audit_aggregate(...)         -> layer counts, ratios and Sparse GPU-Time Coverage (host only)
 """
 from __future__ import annotations
@@ -73,6 +74,8 @@ SIGNATURES = {
     "sp24_tactic_decide": (_i32, [_i32, ctypes.POINTER(_dbl), _i32, ctypes.POINTER(_dbl), _i32,
                                   ctypes.POINTER(Tactic)]),
     "sp24_gemm_kernel": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i64, _i64, _i64]),
+    "sp24_hybrid_gemm": (_i32, [_i32, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "sp24_hybrid_kernel": (ctypes.c_char_p, [_i32, _i32, _i64, _i64, _i64, _i64]),
     "sp24_audit_aggregate": (_i32, [ctypes.POINTER(Tactic), ctypes.POINTER(_i64), _i64, _dbl,
                                     ctypes.POINTER(AuditMetrics)]),
     "sp24_quantize_prune_compress": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp]),
@@ -206,6 +209,25 @@ def dense_gemm(x, w, out_dtype=torch.bfloat16, scale_x=None, scale_w=None, out=N
                           _ptr(out), _stream(x.device))
     _check("dense_gemm", st)
     return out
+
+
+def hybrid_gemm(values, meta, w_dense, x, N_s: int, N_d: int, out_dtype=torch.bfloat16, scale_x=None,
+                scale_w=None, out=None):
+    """Y (M x (N_s + N_d)): columns [0, N_s) from the compressed rows (values, meta), the rest from the
+    dense rows w_dense (N_d x K); one launch.  values / meta / w_dense may be None for an empty region."""
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, N_s + N_d), dtype=out_dtype, device=x.device)
+    st = lib().sp24_hybrid_gemm(_code(x), _code(out), M, N_s, N_d, K, _ptr(values), _ptr(meta), _ptr(w_dense),
+                                _ptr(x), _ptr(scale_x), _ptr(scale_w), _ptr(out), _stream(x.device))
+    _check("sp24_hybrid_gemm", st)
+    return out
+
+
+def hybrid_kernel(in_dtype, out_dtype, M: int, N_s: int, N_d: int, K: int):
+    """Name of the kernel hybrid_gemm launches for this shape; None if rejected."""
+    name = lib().sp24_hybrid_kernel(DTYPE_CODE[in_dtype], DTYPE_CODE[out_dtype], M, N_s, N_d, K)
+    return None if name is None else name.decode()
 
 
 def select_tactic(which, values, meta, dense_other, dense_pruned, M, N, K, out_dtype=torch.bfloat16,

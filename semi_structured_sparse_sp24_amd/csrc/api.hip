@@ -236,6 +236,83 @@ static sp24_status dense_impl(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, in
     return launch_dense_gemm(g, stream, kname) == hipSuccess ? SP24_OK : SP24_E_HIP;
 }
 
+// Dtype and size checks of the hybrid GEMM (no pointer is looked at).
+static sp24_status check_hybrid_shape(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t NS, int64_t ND,
+                                      int64_t K) {
+    if (!is_input_dtype(in_dt) || !out_ok(in_dt, out_dt))
+        return SP24_E_DTYPE;
+    if (NS < 0 || ND < 0 || NS > INT32_MAX / 2 - ND)
+        return SP24_E_SHAPE;
+    // both regions are at most N = NS + ND rows: the plain GEMM's limits cover them
+    sp24_status st = check_shape(in_dt, out_dt, M, NS + ND, K, true);
+    if (st != SP24_OK)
+        return st;
+    if (M > 0 && NS + ND > 0 && NS % 8 != 0)
+        return SP24_E_ALIGN;
+    return SP24_OK;
+}
+
+SP24_API sp24_status sp24_hybrid_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N_s, int64_t N_d,
+                                      int64_t K, const void* values, const uint32_t* meta, const void* W_d,
+                                      const void* X, const float* scale_x, const float* scale_w, void* Y,
+                                      hipStream_t stream) {
+    if (!is_input_dtype(in_dt) || !out_ok(in_dt, out_dt))
+        return SP24_E_DTYPE;
+    if (M < 0 || N_s < 0 || N_d < 0 || K < 0 || K % 4 != 0)
+        return SP24_E_SHAPE;
+    const int64_t N = N_s + N_d;
+    if (M > 0 && N > 0) {
+        if (!Y)
+            return SP24_E_NULL;
+        if (K > 0 && (!X || (N_s > 0 && (!values || !meta)) || (N_d > 0 && !W_d)))
+            return SP24_E_NULL;
+    }
+    sp24_status st = check_hybrid_shape(in_dt, out_dt, M, N_s, N_d, K);
+    if (st != SP24_OK || M == 0 || N == 0)
+        return st;
+    if (!aligned16(Y) || ((uintptr_t)scale_x & 3u) || ((uintptr_t)scale_w & 3u) || !aligned16(X) ||
+        (N_s > 0 && (!aligned16(values) || !aligned16(meta))) || (N_d > 0 && !aligned16(W_d)))
+        return SP24_E_ALIGN;
+    if (K == 0)
+        return launch_fill_zero(Y, M * N * elem_bytes(out_dt), stream) == hipSuccess ? SP24_OK : SP24_E_HIP;
+    HybridArgs h;
+    h.in_dt = in_dt;
+    h.out_dt = out_dt;
+    h.M = M;
+    h.NS = N_s;
+    h.ND = N_d;
+    h.K = K;
+    h.ws_vals = values;
+    h.ws_meta = meta;
+    h.wd = W_d;
+    h.x = X;
+    h.scale_x = scale_x;
+    h.scale_w = scale_w;
+    h.Y = Y;
+    return launch_sp24_hybrid(h, stream, nullptr) == hipSuccess ? SP24_OK : SP24_E_HIP;
+}
+
+SP24_API const char* sp24_hybrid_kernel(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N_s, int64_t N_d,
+                                       int64_t K) {
+    if (M < 0 || K < 0 || K % 4 != 0 || check_hybrid_shape(in_dt, out_dt, M, N_s, N_d, K) != SP24_OK)
+        return nullptr;
+    if (M == 0 || N_s + N_d == 0)
+        return "none";
+    if (K == 0)
+        return "fill_zero";
+    HybridArgs h{};
+    h.in_dt = in_dt;
+    h.out_dt = out_dt;
+    h.M = M;
+    h.NS = N_s;
+    h.ND = N_d;
+    h.K = K;
+    h.dry = true;
+    const char* name = nullptr;
+    launch_sp24_hybrid(h, nullptr, &name);
+    return name;
+}
+
 SP24_API const char* sp24_gemm_kernel(int sparse, sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt,
                                      int64_t M, int64_t N, int64_t K) {
     if (sparse && which != SP24_SPARSE_W && which != SP24_SPARSE_X)

@@ -73,11 +73,41 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-template <sp24_dtype DT, sp24_dtype OUT, class TL>
-__global__ void __launch_bounds__(TL::THREADS, TL::OCC)
-sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const uint8_t* __restrict__ B,
-         const float* __restrict__ sa, const float* __restrict__ sb, void* __restrict__ Y, int RA, int RB,
-         int64_t K, int64_t sya, int64_t syb, int tiles_a, int tiles_b) {
+// The two 2:4 halves of dense A rows, for the dense tiles of the hybrid GEMM:
+// any group of four is the sum of two groups of two, [a b 0 0] + [0 0 c d],
+// and each is a 2:4 group with fixed positions (0, 1) and (2, 3).  q0, q1 are
+// a lane's 32 dense bytes of one step (its SMFMAC lane range of dense K);
+// lo gets the values at positions 0, 1 of every group, hi those at 2, 3.
+template <sp24_dtype DT>
+__device__ __forceinline__ void split_halves(const uint4& q0, const uint4& q1, uint4& lo, uint4& hi) {
+    if constexpr (DT == SP24_E4M3) {
+        // a group is one dword: bytes 0, 1 and bytes 2, 3
+        lo = make_uint4(__builtin_amdgcn_perm(q0.y, q0.x, 0x05040100u), __builtin_amdgcn_perm(q0.w, q0.z, 0x05040100u),
+                        __builtin_amdgcn_perm(q1.y, q1.x, 0x05040100u), __builtin_amdgcn_perm(q1.w, q1.z, 0x05040100u));
+        hi = make_uint4(__builtin_amdgcn_perm(q0.y, q0.x, 0x07060302u), __builtin_amdgcn_perm(q0.w, q0.z, 0x07060302u),
+                        __builtin_amdgcn_perm(q1.y, q1.x, 0x07060302u), __builtin_amdgcn_perm(q1.w, q1.z, 0x07060302u));
+    } else {
+        // a group is two dwords: the first holds positions 0, 1, the second 2, 3
+        lo = make_uint4(q0.x, q0.z, q1.x, q1.z);
+        hi = make_uint4(q0.y, q0.w, q1.y, q1.w);
+    }
+}
+
+// One output tile of the GEMM, D[a][b] for a in [a0, a0 + rows), b in
+// [b0, b0 + TL::BB), over the whole K.  DENSE == false: A is compressed
+// (values + metadata), tile rows TL::BA.  DENSE == true: A is dense and the
+// tile has TL::BA / 2 rows, so that a step of dense A takes the bytes of a
+// compressed step; each fragment runs two SMFMACs, one per 2:4 half, with
+// constant positions.  The pipeline, the B side and the epilogue are the same.
+// Y, sa and RA refer to this tile's region of A rows; `group` is the tile's
+// group of tile-sharing workgroups (it sets the K rotation).
+template <sp24_dtype DT, sp24_dtype OUT, class TL, bool DENSE>
+__device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a2s, uint8_t* b0s, uint8_t* b1s,
+                                          uint8_t* b2s, uint8_t* m0s, uint8_t* m1s, uint8_t* m2s,
+                                          const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
+                                          const uint8_t* __restrict__ B, const float* __restrict__ sa,
+                                          const float* __restrict__ sb, void* __restrict__ Y, int RA, int RB,
+                                          int64_t K, int64_t sya, int64_t syb, int a0, int b0, int group) {
     using L = StepLayout<DT>;
     using Op = SparseOp<DT>;
     constexpr int MWS = L::META_WORDS;                  // metadata words per row per step: 2 or 4
@@ -85,49 +115,44 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
     // for fp8), one 16-byte load per row -- a request per row per block where
     // per-step 4-byte loads cost a request per row per step
     constexpr int T = 4 / MWS;
-    constexpr int kBA = TL::BA, kBB = TL::BB, kWB = TL::WB, kWaves = TL::WAVES, kFA = TL::FA, kFB = TL::FB;
+    constexpr int kBA = DENSE ? TL::BA / 2 : TL::BA;    // A rows of this tile
+    constexpr int kBB = TL::BB, kWB = TL::WB, kWaves = TL::WAVES, kFB = TL::FB;
+    constexpr int kFA = kBA / 16 / TL::WA;
     constexpr int kAStage = TL::A_STAGE, kBStage = TL::B_STAGE, kMBlock = TL::M_BLOCK;
     constexpr int M_WAVES = kMBlock / 1024;             // waves that issue a block's 1 KiB loads
     constexpr int A_LOADS = kAStage / 1024 / kWaves;    // per wave
     constexpr int B_LOADS = kBStage / 1024 / kWaves;    // per wave
     static_assert(A_LOADS * kWaves * 1024 == kAStage && B_LOADS * kWaves * 1024 == kBStage, "whole loads per wave");
     static_assert(M_WAVES * 1024 == kMBlock && M_WAVES <= kWaves, "metadata block");
+    static_assert(kFA >= 1, "fragments per wave");
+    // a dense A step is a B-sized row step: the stage then holds kBA rows of it
+    constexpr int A_ROW_STEP = DENSE ? L::B_STEP_BYTES : L::A_STEP_BYTES;
+    static_assert(kBA * A_ROW_STEP == kAStage, "dense rows fill the A stage");
+    constexpr int A_CH = A_ROW_STEP / 16;               // 16-byte chunks per row step: 4, or 8 dense
+    constexpr bool META = !DENSE;
     constexpr int AB = A_LOADS + B_LOADS;
     constexpr int U = 3 * T;                            // loop unroll: a whole number of stages and blocks
-
-    __shared__ __attribute__((aligned(1024))) uint8_t a0s[kAStage], a1s[kAStage], a2s[kAStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t b0s[kBStage], b1s[kBStage], b2s[kBStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t m0s[kMBlock], m1s[kMBlock], m2s[kMBlock];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int r = lane & 15, kg = lane >> 4;
     const int wa = wave / kWB, wb = wave % kWB;
 
-    // ---- tile order: XCD-aware, grouped 4 A tiles x all B tiles
-    const int nwg = gridDim.x;
-    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    const int per_xcd = (nwg + 7) >> 3, full = nwg & 7 ? (nwg & 7) : 8;   // XCDs holding per_xcd tiles
-    const int t = xcd < full ? xcd * per_xcd + local : full * per_xcd + (xcd - full) * (per_xcd - 1) + local;
-    constexpr int G = 8;
-    const int group = t / (G * tiles_b), within = t - group * G * tiles_b;
-    const int g_rows = min(G, tiles_a - group * G);
-    const int ta = group * G + within % g_rows, tb = within / g_rows;
-    const int a0 = ta * kBA, b0 = tb * kBB;
-
     const int steps = (int)(K / L::KSTEP);
-    const uint32_t a_row_bytes = (uint32_t)(K / 2 * L::ELEM), b_row_bytes = (uint32_t)(K * L::ELEM);
+    const uint32_t a_row_bytes = (uint32_t)(DENSE ? K * L::ELEM : K / 2 * L::ELEM);
+    const uint32_t b_row_bytes = (uint32_t)(K * L::ELEM);
     const uint32_t m_row_bytes = (uint32_t)(K / 8);
     const Buf bufA(av, (uint32_t)RA * a_row_bytes);     // rows past RA / RB read as zeros
-    const Buf bufM(am, (uint32_t)RA * m_row_bytes);
+    const Buf bufM(am, META ? (uint32_t)RA * m_row_bytes : 0u);
     const Buf bufB(B, (uint32_t)RB * b_row_bytes);
 
     // ---- per-lane global offsets of this wave's loads (step 0), and LDS slots
     uint32_t ga[A_LOADS], gb[B_LOADS];
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
-        const int row = 16 * (A_LOADS * wave + j) + (lane >> 2);
-        const int c = (lane & 3) ^ ((row >> 1) & 3);             // chunk stored in slot lane & 3
+        // a 1 KiB load covers 1024 / A_ROW_STEP rows; chunk c of a row lands in slot c ^ swizzle(row)
+        const int row = (1024 / A_ROW_STEP) * (A_LOADS * wave + j) + lane / A_CH;
+        const int c = (lane % A_CH) ^ ((row >> 1) & (A_CH - 1));
         ga[j] = (uint32_t)(a0 + row) * a_row_bytes + 16 * c;
     }
 #pragma unroll
@@ -150,7 +175,7 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
         int s = sl + rot;
         s = s >= steps ? s - steps : s;
         const bool live = sl < steps;
-        const uint32_t sA = live ? (uint32_t)s * L::A_STEP_BYTES : kOOB;
+        const uint32_t sA = live ? (uint32_t)s * A_ROW_STEP : kOOB;
         const uint32_t sB = live ? (uint32_t)s * L::B_STEP_BYTES : kOOB;
         if (do_a) {
 #pragma unroll
@@ -163,7 +188,7 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
                 dma16(bufB, bs + 1024 * (B_LOADS * wave + j), gb[j], sB);
             // the block of steps s .. s + T - 1 (with T = 2 and an odd step count,
             // the last block's second half is past the row: read, never used)
-            if (ms != nullptr && wave < M_WAVES)
+            if (META && ms != nullptr && wave < M_WAVES)
                 dma16(bufM, ms + 1024 * wave, gm, live ? (uint32_t)s * (4 * MWS) : kOOB);
         }
     };
@@ -171,18 +196,25 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
     // before computing step x: this wave's loads of step x have landed when
     // only those of step x + 1 (issued one step later) may be outstanding
     auto wait_step = [&](bool next_has_meta) {
-        if (next_has_meta && wave < M_WAVES)
+        if (META && next_has_meta && wave < M_WAVES)
             wait_vmcnt_lgkm0<AB + 1>();
         else
             wait_vmcnt_lgkm0<AB>();
     };
 
     // ---- fragment read offsets (bytes within a stage / a metadata block)
-    const int a_frag = (wa * 16 * kFA + r) * 64 + 16 * (kg ^ ((r >> 1) & 3));
-    const int m_frag = (wa * 16 * kFA + r) * 16 + 4 * L::meta_word(kg);
+    const int a_row = wa * 16 * kFA + r;
+    const int a_frag = a_row * 64 + 16 * (kg ^ ((r >> 1) & 3));
+    // dense rows: the lane's 32 bytes are chunks 2 kg and 2 kg + 1 of its row
+    const int a_frag_d0 = a_row * 128 + 16 * ((2 * kg) ^ ((r >> 1) & 7));
+    const int a_frag_d1 = a_row * 128 + 16 * ((2 * kg + 1) ^ ((r >> 1) & 7));
+    const int m_frag = a_row * 16 + 4 * L::meta_word(kg);
     const int msh = L::meta_shift(kg);
     const int b_frag0 = (wb * 16 * kFB + r) * 128 + 16 * (kg ^ ((r >> 1) & 7));
     const int b_frag1 = (wb * 16 * kFB + r) * 128 + 16 * ((4 + kg) ^ ((r >> 1) & 7));
+    // positions (0, 1) and (2, 3) in every group: nibbles 0x4 and 0xE
+    constexpr uint32_t kIdxLo = L::ELEM == 2 ? 0x4444u : 0x44444444u;
+    constexpr uint32_t kIdxHi = L::ELEM == 2 ? 0xEEEEu : 0xEEEEEEEEu;
 
     f32x4 acc[kFA][kFB];
 #pragma unroll
@@ -192,13 +224,19 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
             acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     // u: the step's position within its metadata block
-    uint4 fa[kFA];
+    uint4 fa[kFA], fh[DENSE ? kFA : 1];
     uint32_t fi[kFA];
     auto load_a = [&](const uint8_t* as, const uint8_t* ms, int u) {
 #pragma unroll
         for (int i = 0; i < kFA; ++i) {
-            fa[i] = *reinterpret_cast<const uint4*>(as + a_frag + i * 16 * 64);
-            fi[i] = *reinterpret_cast<const uint32_t*>(ms + m_frag + 4 * MWS * u + i * 16 * 16) >> msh;
+            if constexpr (DENSE) {
+                const uint4 q0 = *reinterpret_cast<const uint4*>(as + a_frag_d0 + i * 16 * 128);
+                const uint4 q1 = *reinterpret_cast<const uint4*>(as + a_frag_d1 + i * 16 * 128);
+                split_halves<DT>(q0, q1, fa[i], fh[i]);
+            } else {
+                fa[i] = *reinterpret_cast<const uint4*>(as + a_frag + i * 16 * 64);
+                fi[i] = *reinterpret_cast<const uint32_t*>(ms + m_frag + 4 * MWS * u + i * 16 * 16) >> msh;
+            }
         }
     };
     // One step's MFMAs, the B fragments read one column ahead of their use
@@ -218,8 +256,14 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
             if (j == kFB / 2)
                 issue_bm();
 #pragma unroll
-            for (int i = 0; i < kFA; ++i)
-                acc[i][j] = Op::mma(fa[i], b0[j & 1], b1[j & 1], fi[i], acc[i][j]);
+            for (int i = 0; i < kFA; ++i) {
+                if constexpr (DENSE) {
+                    acc[i][j] = Op::mma(fa[i], b0[j & 1], b1[j & 1], kIdxLo, acc[i][j]);
+                    acc[i][j] = Op::mma(fh[i], b0[j & 1], b1[j & 1], kIdxHi, acc[i][j]);
+                } else {
+                    acc[i][j] = Op::mma(fa[i], b0[j & 1], b1[j & 1], fi[i], acc[i][j]);
+                }
+            }
         }
     };
 
@@ -278,6 +322,62 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
     }
 }
 
+// Tile t (the workgroup's place in an XCD-aware order: consecutive t run on
+// one XCD) -> (group, A tile, B tile), in groups of G A tiles x all B tiles.
+struct TilePos {
+    int group, ta, tb;
+};
+__device__ __forceinline__ int xcd_order(int nwg) {
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int per_xcd = (nwg + 7) >> 3, full = nwg & 7 ? (nwg & 7) : 8;   // XCDs holding per_xcd tiles
+    return xcd < full ? xcd * per_xcd + local : full * per_xcd + (xcd - full) * (per_xcd - 1) + local;
+}
+__device__ __forceinline__ TilePos tile_pos(int t, int tiles_a, int tiles_b) {
+    constexpr int G = 8;
+    const int group = t / (G * tiles_b), within = t - group * G * tiles_b;
+    const int g_rows = min(G, tiles_a - group * G);
+    return {group, group * G + within % g_rows, within / g_rows};
+}
+
+#define SP24_TILE_LDS(TL)                                                                                    \
+    __shared__ __attribute__((aligned(1024))) uint8_t a0s[TL::A_STAGE], a1s[TL::A_STAGE], a2s[TL::A_STAGE]; \
+    __shared__ __attribute__((aligned(1024))) uint8_t b0s[TL::B_STAGE], b1s[TL::B_STAGE], b2s[TL::B_STAGE]; \
+    __shared__ __attribute__((aligned(1024))) uint8_t m0s[TL::M_BLOCK], m1s[TL::M_BLOCK], m2s[TL::M_BLOCK]
+
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
+__global__ void __launch_bounds__(TL::THREADS, TL::OCC)
+sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const uint8_t* __restrict__ B,
+         const float* __restrict__ sa, const float* __restrict__ sb, void* __restrict__ Y, int RA, int RB,
+         int64_t K, int64_t sya, int64_t syb, int tiles_a, int tiles_b) {
+    SP24_TILE_LDS(TL);
+    const TilePos p = tile_pos(xcd_order(gridDim.x), tiles_a, tiles_b);
+    tile_body<DT, OUT, TL, false>(a0s, a1s, a2s, b0s, b1s, b2s, m0s, m1s, m2s, av, am, B, sa, sb, Y, RA, RB, K,
+                                  sya, syb, p.ta * TL::BA, p.tb * TL::BB, p.group);
+}
+
+// The hybrid GEMM in one launch: the first tiles_s * tiles_b workgroups (in
+// the XCD-aware order) take the compressed rows [0, RS) of A, the rest the
+// dense rows [0, RD) of Ad, whose outputs start at Yd (scales at sd); both
+// share B, its scales and the output strides.
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
+__global__ void __launch_bounds__(TL::THREADS, TL::OCC)
+sp24_hybrid(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const uint8_t* __restrict__ ad,
+            const uint8_t* __restrict__ B, const float* __restrict__ sa, const float* __restrict__ sd,
+            const float* __restrict__ sb, void* __restrict__ Y, void* __restrict__ Yd, int RS, int RD, int RB,
+            int64_t K, int64_t sya, int64_t syb, int tiles_s, int tiles_d, int tiles_b) {
+    SP24_TILE_LDS(TL);
+    const int t = xcd_order(gridDim.x);
+    if (t < tiles_s * tiles_b) {
+        const TilePos p = tile_pos(t, tiles_s, tiles_b);
+        tile_body<DT, OUT, TL, false>(a0s, a1s, a2s, b0s, b1s, b2s, m0s, m1s, m2s, av, am, B, sa, sb, Y, RS, RB, K,
+                                      sya, syb, p.ta * TL::BA, p.tb * TL::BB, p.group);
+    } else {
+        const TilePos p = tile_pos(t - tiles_s * tiles_b, tiles_d, tiles_b);
+        tile_body<DT, OUT, TL, true>(a0s, a1s, a2s, b0s, b1s, b2s, m0s, m1s, m2s, ad, nullptr, B, sd, sb, Yd, RD,
+                                     RB, K, sya, syb, p.ta * (TL::BA / 2), p.tb * TL::BB, p.group);
+    }
+}
+
 template <sp24_dtype DT, sp24_dtype OUT, class TL>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s, const char** kname, const char* name) {
     const int RA = (int)(g.a_is_w ? g.N : g.M);
@@ -316,6 +416,45 @@ hipError_t launch_big(const GemmArgs& g, hipStream_t s, const char** kname) {
     return launch_tile<DT, OUT, T128x64>(g, s, kname, "sp24_big_128x64");
 }
 
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
+hipError_t launch_hybrid_tile(const HybridArgs& h, hipStream_t s, const char** kname, const char* name) {
+    const int RS = (int)h.NS, RD = (int)h.ND, RB = (int)h.M;
+    const int tiles_s = (RS + TL::BA - 1) / TL::BA, tiles_d = (RD + TL::BA / 2 - 1) / (TL::BA / 2);
+    const int tiles_b = (RB + TL::BB - 1) / TL::BB;
+    if (kname)
+        *kname = name;
+    if (h.dry)
+        return hipSuccess;
+    void* Yd = (uint8_t*)h.Y + h.NS * elem_bytes(OUT);
+    hipLaunchKernelGGL((sp24_hybrid<DT, OUT, TL>), dim3((tiles_s + tiles_d) * tiles_b), dim3(TL::THREADS), 0, s,
+                       (const uint8_t*)h.ws_vals, h.ws_meta, (const uint8_t*)h.wd, (const uint8_t*)h.x, h.scale_w,
+                       h.scale_w ? h.scale_w + h.NS : nullptr, h.scale_x, h.Y, Yd, RS, RD, RB, h.K, (int64_t)1,
+                       h.NS + h.ND, tiles_s, tiles_d, tiles_b);
+    return hipGetLastError();
+}
+
+template <class TL>
+int64_t hybrid_tiles_of(const HybridArgs& h) {
+    const int64_t ts = (h.NS + TL::BA - 1) / TL::BA, td = (h.ND + TL::BA / 2 - 1) / (TL::BA / 2);
+    return (ts + td) * ((h.M + TL::BB - 1) / TL::BB) * TL::OCC;
+}
+
+// The tile choice of the plain GEMM, counting the dense region's half-height tiles.
+template <sp24_dtype DT, sp24_dtype OUT>
+hipError_t launch_hybrid(const HybridArgs& h, hipStream_t s, const char** kname) {
+    constexpr int64_t kFill = 192;
+    if (h.M > 64) {
+        if (hybrid_tiles_of<T256x256>(h) >= kFill)
+            return launch_hybrid_tile<DT, OUT, T256x256>(h, s, kname, "sp24_hybrid_256x256");
+        if (hybrid_tiles_of<T256x128>(h) >= kFill)
+            return launch_hybrid_tile<DT, OUT, T256x128>(h, s, kname, "sp24_hybrid_256x128");
+        return launch_hybrid_tile<DT, OUT, T128x128>(h, s, kname, "sp24_hybrid_128x128");
+    }
+    if (hybrid_tiles_of<T256x64>(h) >= kFill)
+        return launch_hybrid_tile<DT, OUT, T256x64>(h, s, kname, "sp24_hybrid_256x64");
+    return launch_hybrid_tile<DT, OUT, T128x64>(h, s, kname, "sp24_hybrid_128x64");
+}
+
 }  // namespace
 
 hipError_t launch_sp24_gemm_big(const GemmArgs& g, hipStream_t s, const char** kname) {
@@ -331,6 +470,24 @@ hipError_t launch_sp24_gemm_big(const GemmArgs& g, hipStream_t s, const char** k
     case SP24_E4M3:
         if (g.out_dt == SP24_BF16) return launch_big<SP24_E4M3, SP24_BF16>(g, s, kname);
         return launch_big<SP24_E4M3, SP24_F32>(g, s, kname);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_sp24_hybrid(const HybridArgs& h, hipStream_t s, const char** kname) {
+    switch (h.in_dt) {
+    case SP24_BF16:
+        if (h.out_dt == SP24_BF16) return launch_hybrid<SP24_BF16, SP24_BF16>(h, s, kname);
+        if (h.out_dt == SP24_F16) return launch_hybrid<SP24_BF16, SP24_F16>(h, s, kname);
+        return launch_hybrid<SP24_BF16, SP24_F32>(h, s, kname);
+    case SP24_F16:
+        if (h.out_dt == SP24_F16) return launch_hybrid<SP24_F16, SP24_F16>(h, s, kname);
+        if (h.out_dt == SP24_BF16) return launch_hybrid<SP24_F16, SP24_BF16>(h, s, kname);
+        return launch_hybrid<SP24_F16, SP24_F32>(h, s, kname);
+    case SP24_E4M3:
+        if (h.out_dt == SP24_BF16) return launch_hybrid<SP24_E4M3, SP24_BF16>(h, s, kname);
+        return launch_hybrid<SP24_E4M3, SP24_F32>(h, s, kname);
     default:
         return hipErrorInvalidValue;
     }

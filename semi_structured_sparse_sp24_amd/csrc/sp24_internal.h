@@ -59,6 +59,22 @@ hipError_t launch_sp24_gemm(const GemmArgs& g, hipStream_t s, const char** kname
 // with more than 16 dense rows (called by launch_sp24_gemm).
 hipError_t launch_sp24_gemm_big(const GemmArgs& g, hipStream_t s, const char** kname);
 
+// The hybrid GEMM: Y (M x (NS + ND)), columns [0, NS) = X * Ws^T with Ws
+// compressed, columns [NS, NS + ND) = X * Wd^T with Wd dense; one launch.
+struct HybridArgs {
+    sp24_dtype in_dt, out_dt;
+    int64_t M, NS, ND, K;
+    const void* ws_vals;      // NS x K/2
+    const uint32_t* ws_meta;  // NS x K/32
+    const void* wd;           // ND x K
+    const void* x;            // M x K
+    const float* scale_x;     // M, or null
+    const float* scale_w;     // NS + ND, or null
+    void* Y;
+    bool dry = false;
+};
+hipError_t launch_sp24_hybrid(const HybridArgs& h, hipStream_t s, const char** kname);
+
 struct DenseArgs {
     sp24_dtype in_dt, out_dt;
     int64_t M, N, K;

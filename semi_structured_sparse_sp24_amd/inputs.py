@@ -52,7 +52,17 @@ WORKLOADS = {
     "online": dict(index=5, dtype=BF16, out=BF16, shapes=[(4096, 4096)], ms=[4096]),
     "online_fp8": dict(index=6, dtype=E4M3, act=BF16, out=BF16, shapes=[(4096, 4096), (28672, 4096)],
                        ms=[4096]),
+    # the prefill layers with one output row in eight kept dense (hybrid_split)
+    "hybrid": dict(index=7, dtype=BF16, out=BF16,
+                   shapes=[(4096, 4096), (6144, 4096), (28672, 4096), (4096, 14336)], ms=[2048, 8192]),
 }
+
+
+def hybrid_split(N: int) -> tuple[int, int]:
+    """(sparse rows, dense rows) of an N-row weight in the hybrid workload: the
+    last N/8 rows (a multiple of 256) stay dense."""
+    nd = max(256, N // 8 // 256 * 256)
+    return N - nd, nd
 
 
 def seed_of(c: int, s: int, t: int, j: int) -> int:

@@ -239,3 +239,28 @@ def test_block_manifest_layout():
                                                               "reason": "Alignment failure"}
     assert m["layers"]["model.layers.0.mlp.gate_up_proj"] == {"eligible": True, "selected": "sparse"}
     assert "reason" in m["layers"]["model.layers.5.mlp.down_proj"]
+
+
+def test_hybrid_validation_precedes_hip():
+    f = sp.lib().sp24_hybrid_gemm
+    ok = dict(dt=sp.BF16, out=sp.BF16, M=4, NS=16, ND=8, K=64, v=16, m=32, wd=48, x=64, sx=None, sw=None, y=80)
+
+    def h(**kw):
+        a = {**ok, **kw}
+        return f(a["dt"], a["out"], a["M"], a["NS"], a["ND"], a["K"], a["v"], a["m"], a["wd"], a["x"], a["sx"],
+                 a["sw"], a["y"], None)
+    assert h(dt=sp.F32) == 3 and h(dt=sp.E4M3, out=sp.F16) == 3
+    assert h(M=-1) == 2 and h(NS=-8) == 2 and h(ND=-1) == 2 and h(K=62) == 2
+    assert h(M=0) == 0 and h(NS=0, ND=0) == 0
+    assert h(y=None) == 1 and h(x=None) == 1 and h(v=None) == 1 and h(m=None) == 1 and h(wd=None) == 1
+    assert h(K=96) == 4 and h(dt=sp.E4M3, K=64) == 4           # whole sparse steps for both regions
+    assert h(NS=12) == 4                                       # dense outputs start on a 16-byte boundary
+    assert h(x=72) == 4 and h(wd=56) == 4 and h(y=88) == 4 and h(sw=66) == 4
+    k = sp.hybrid_kernel
+    bf = __import__("torch").bfloat16
+    assert k(bf, bf, 4096, 4096, 1024, 4096) == "sp24_hybrid_256x256"
+    assert k(bf, bf, 64, 4096, 512, 4096) == "sp24_hybrid_128x64"
+    assert k(bf, bf, 64, 49152, 512, 4096) == "sp24_hybrid_256x64"
+    assert k(bf, bf, 512, 512, 256, 4096) == "sp24_hybrid_128x128"
+    assert k(bf, bf, 0, 16, 8, 64) == "none" and k(bf, bf, 4, 16, 8, 0) == "fill_zero"
+    assert k(bf, bf, 4, 12, 8, 64) is None and k(bf, bf, 4, 16, 8, 96) is None
