@@ -19,7 +19,7 @@ such blocks per M (its metrics in the line; --manifest-dir writes it whole).
 One JSON line is printed.
 
 Workloads (default: decode, the bf16 Llama-3-8B-like decode layers):
-  tiny | decode | prefill | fp8 | online | online_fp8 | hybrid
+  tiny | decode | prefill | fp8 | int8 | online | online_fp8 | hybrid
 """
 from __future__ import annotations
 
@@ -39,10 +39,12 @@ import semi_structured_sparse_sp24_amd as sp  # noqa: E402
 from semi_structured_sparse_sp24_amd import audit, inputs  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-SPARSE_PEAK_TFLOPS = {inputs.BF16: 5033.0, inputs.F16: 5033.0, inputs.E4M3: 10066.0}   # 2:4, dense-equivalent
-DENSE_PEAK_TFLOPS = {inputs.BF16: 2516.0, inputs.F16: 2516.0, inputs.E4M3: 5033.0}
-DTYPE_NAME = {inputs.F16: "f16", inputs.BF16: "bf16", inputs.E4M3: "e4m3"}
-TORCH = {inputs.F16: torch.float16, inputs.BF16: torch.bfloat16, inputs.E4M3: torch.float8_e4m3fn}
+# published MI355X dense peaks (int8 in TOP/s), and twice that for 2:4, counted dense-equivalent
+SPARSE_PEAK_TFLOPS = {inputs.BF16: 5033.0, inputs.F16: 5033.0, inputs.E4M3: 10066.0, inputs.I8: 10066.0}
+DENSE_PEAK_TFLOPS = {inputs.BF16: 2516.0, inputs.F16: 2516.0, inputs.E4M3: 5033.0, inputs.I8: 5033.0}
+DTYPE_NAME = {inputs.F16: "f16", inputs.BF16: "bf16", inputs.E4M3: "e4m3", inputs.I8: "i8"}
+TORCH = {inputs.F16: torch.float16, inputs.BF16: torch.bfloat16, inputs.E4M3: torch.float8_e4m3fn,
+         inputs.I8: torch.int8}
 
 
 def dev(bits, dt):
@@ -397,8 +399,8 @@ def main():
     w = inputs.WORKLOADS[workload]
     dt, out = w["dtype"], w["out"]
     eb, out_eb = inputs.ELEM_BYTES[dt], inputs.ELEM_BYTES[out]
-    cold = (workload in ("decode", "fp8", "tiny")) if args.cold == "auto" else args.cold == "on"
-    scales = dt == inputs.E4M3
+    cold = (workload in ("decode", "fp8", "int8", "tiny")) if args.cold == "auto" else args.cold == "on"
+    scales = dt in (inputs.E4M3, inputs.I8)
 
     cases = build_cases(workload, cold)
     runner = Runner(chains(workload, cases))

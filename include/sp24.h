@@ -64,7 +64,8 @@ typedef enum {
     SP24_F16 = 0,   /* IEEE binary16 */
     SP24_BF16 = 1,  /* bfloat16 */
     SP24_E4M3 = 2,  /* OCP FP8 E4M3 (e4m3fn) */
-    SP24_F32 = 3    /* binary32: an output dtype only */
+    SP24_F32 = 3,   /* binary32: an output dtype only */
+    SP24_I8 = 4     /* two's complement int8 (quantized, with per-row scales) */
 } sp24_dtype;
 
 typedef enum {
@@ -97,7 +98,8 @@ int64_t sp24_meta_words_per_row(int64_t K);
  * "How 2:4 sparsity works": half-size values plus a 2-bit index per kept
  * value).  One pass: the dense operand is read once, values and meta are
  * written once (the fused form of the paper's section 3.5).
- *   dt      SP24_F16, SP24_BF16 or SP24_E4M3
+ *   dt      SP24_F16, SP24_BF16, SP24_E4M3 or SP24_I8 (for int8 the magnitude
+ *           is |x|, so -128 ranks above 127)
  *   rows, K dense operand is rows x K; K % 4 == 0; rows, K >= 0 (0 is a no-op)
  *   src     rows x K, row stride ld_src elements (ld_src >= K)
  *   values  out: rows x K/2 elements (dt), row stride K/2
@@ -163,14 +165,17 @@ sp24_status sp24_quantize_e4m3(sp24_dtype src_dt, int64_t rows, int64_t K,
  *   which     SP24_SPARSE_W: (values, meta) is W (N x K) compressed and
  *             `dense` is X (M x K).  SP24_SPARSE_X: (values, meta) is X
  *             compressed and `dense` is W.
- *   in_dt     SP24_F16, SP24_BF16 or SP24_E4M3 (both operands)
+ *   in_dt     SP24_F16, SP24_BF16, SP24_E4M3 or SP24_I8 (both operands; int8
+ *             products accumulate exactly in int32, converted to fp32 before
+ *             the scales: the 2:4 + INT8 variant of the 2:4-versus-
+ *             quantization paper, section 4.2 "Speed")
  *   out_dt    SP24_F16 or SP24_BF16 or SP24_F32 for 16-bit inputs;
- *             SP24_BF16 or SP24_F32 for SP24_E4M3
- *   M, N, K   M, N >= 0; K % 64 == 0 (16-bit) or K % 128 == 0 (fp8), else
+ *             SP24_BF16 or SP24_F32 for SP24_E4M3 and SP24_I8
+ *   M, N, K   M, N >= 0; K % 64 == 0 (16-bit) or K % 128 == 0 (8-bit), else
  *             SP24_E_ALIGN: the shape is not eligible and the caller runs
  *             dense_gemm instead (a visible fallback, never a silent one)
- *   scale_x   M fp32 per-token scales, or NULL (= 1); used with fp8 inputs
- *   scale_w   N fp32 per-channel scales, or NULL (= 1); used with fp8 inputs
+ *   scale_x   M fp32 per-token scales, or NULL (= 1); used with 8-bit inputs
+ *   scale_w   N fp32 per-channel scales, or NULL (= 1); used with 8-bit inputs
  *   Y         out: M x N of out_dt, row stride N
  *   All pointers 16-byte aligned.
  */

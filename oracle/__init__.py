@@ -20,7 +20,7 @@ import os
 
 import numpy as np
 
-F16, BF16, E4M3, F32 = 0, 1, 2, 3
+F16, BF16, E4M3, F32, I8 = 0, 1, 2, 3, 4
 SPARSE_W, SPARSE_X = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -99,7 +99,7 @@ class use_library:
 
 
 def _bits_dtype(dt: int):
-    return {F16: np.uint16, BF16: np.uint16, E4M3: np.uint8, F32: np.uint32}[dt]
+    return {F16: np.uint16, BF16: np.uint16, E4M3: np.uint8, F32: np.uint32, I8: np.uint8}[dt]
 
 
 def _ptr(a):

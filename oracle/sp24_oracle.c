@@ -38,6 +38,8 @@
  *   - dropped positions decompress to +0.0 (bit pattern 0);
  *   - fp8 is OCP E4M3 ("e4m3fn": no Inf, 0x7F/0xFF are NaN, max 448) with one
  *     fp32 scale per row of each operand, applied to the fp64 result;
+ *   - int8 is two's complement, its magnitude |x| (-128 ranks above 127),
+ *     with per-row fp32 scales as for fp8;
  *   - fused online fp8 path: per-row scale max|x| / 448 and codes e4m3(x / s)
  *     rounded to nearest even and saturated at 448, both in fp32; pruning
  *     acts on the codes (quantize first, then prune).
@@ -47,7 +49,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F16 = 0, OR_BF16 = 1, OR_E4M3 = 2, OR_F32 = 3 };
+enum { OR_F16 = 0, OR_BF16 = 1, OR_E4M3 = 2, OR_F32 = 3, OR_I8 = 4 };
 enum { OR_SPARSE_W = 0, OR_SPARSE_X = 1 };
 enum { OR_OK = 0, OR_E_ARG = 1 };
 
@@ -116,6 +118,7 @@ static double decode_elem(int dt, const void *base, int64_t i)
     case OR_BF16: return oracle_decode_bf16(((const uint16_t *)base)[i]);
     case OR_E4M3: return oracle_decode_e4m3(((const uint8_t *)base)[i]);
     case OR_F32:  return oracle_decode_f32(((const uint32_t *)base)[i]);
+    case OR_I8:   return (double)((const int8_t *)base)[i];     /* two's complement */
     }
     return NAN;
 }
@@ -205,20 +208,25 @@ void oracle_encode_array(int dt, const double *src, int64_t n, void *out)
 
 static int elem_bytes(int dt)
 {
-    return dt == OR_E4M3 ? 1 : (dt == OR_F32 ? 4 : 2);
+    return dt == OR_E4M3 || dt == OR_I8 ? 1 : (dt == OR_F32 ? 4 : 2);
 }
 
 /* Raw bit pattern of element i. */
 static uint32_t elem_bits(int dt, const void *base, int64_t i)
 {
-    if (dt == OR_E4M3)
+    if (dt == OR_E4M3 || dt == OR_I8)
         return ((const uint8_t *)base)[i];
     return ((const uint16_t *)base)[i];
 }
 
-/* Magnitude key: the bit pattern with the sign bit cleared. */
+/* Magnitude key: the bit pattern with the sign bit cleared (sign-magnitude
+ * float formats), or |x| for two's complement int8 (-128 -> 128). */
 static uint32_t magnitude_key(int dt, uint32_t bits)
 {
+    if (dt == OR_I8) {
+        int v = (int8_t)(uint8_t)bits;
+        return (uint32_t)(v < 0 ? -v : v);
+    }
     return dt == OR_E4M3 ? (bits & 0x7f) : (bits & 0x7fff);
 }
 
@@ -253,7 +261,7 @@ int64_t oracle_meta_words_per_row(int64_t K) { return (K + 31) / 32; }
 int oracle_prune_compress(int dt, int64_t rows, int64_t K, const void *src,
                           int64_t ld_src, void *values, uint32_t *meta)
 {
-    if (dt != OR_F16 && dt != OR_BF16 && dt != OR_E4M3)
+    if (dt != OR_F16 && dt != OR_BF16 && dt != OR_E4M3 && dt != OR_I8)
         return OR_E_ARG;
     if (rows < 0 || K < 0 || K % 4 != 0 || ld_src < K)
         return OR_E_ARG;
@@ -286,7 +294,7 @@ int oracle_prune_compress(int dt, int64_t rows, int64_t K, const void *src,
 int oracle_decompress(int dt, int64_t rows, int64_t K, const void *values,
                       const uint32_t *meta, void *dst, int64_t ld_dst)
 {
-    if (dt != OR_F16 && dt != OR_BF16 && dt != OR_E4M3)
+    if (dt != OR_F16 && dt != OR_BF16 && dt != OR_E4M3 && dt != OR_I8)
         return OR_E_ARG;
     if (rows < 0 || K < 0 || K % 4 != 0 || ld_dst < K)
         return OR_E_ARG;
@@ -390,7 +398,7 @@ int oracle_gemm(int dt, int64_t M, int64_t N, int64_t K,
                 const float *scale_x, const float *scale_w,
                 const int64_t *mrows, int64_t nm, double *R)
 {
-    if (dt != OR_F16 && dt != OR_BF16 && dt != OR_E4M3)
+    if (dt != OR_F16 && dt != OR_BF16 && dt != OR_E4M3 && dt != OR_I8)
         return OR_E_ARG;
     if (M < 0 || N < 0 || K < 0 || K % 4 != 0 || nm < 0)
         return OR_E_ARG;

@@ -25,7 +25,7 @@ import os
 
 import torch
 
-F16, BF16, E4M3, F32 = 0, 1, 2, 3
+F16, BF16, E4M3, F32, I8 = 0, 1, 2, 3, 4
 SPARSE_W, SPARSE_X = 0, 1
 STATUS = {0: "SP24_OK", 1: "SP24_E_NULL", 2: "SP24_E_SHAPE", 3: "SP24_E_DTYPE", 4: "SP24_E_ALIGN",
           5: "SP24_E_HIP"}
@@ -112,7 +112,8 @@ def _check(fn, st):
         raise Sp24Error(fn, st)
 
 
-DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3, torch.float32: F32}
+DTYPE_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3, torch.float32: F32,
+              torch.int8: I8}
 CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 
 

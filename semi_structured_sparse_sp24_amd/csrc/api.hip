@@ -29,10 +29,10 @@ hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
-bool is_input_dtype(int dt) { return dt == SP24_F16 || dt == SP24_BF16 || dt == SP24_E4M3; }
+bool is_input_dtype(int dt) { return dt == SP24_F16 || dt == SP24_BF16 || dt == SP24_E4M3 || dt == SP24_I8; }
 
 bool out_ok(sp24_dtype in, sp24_dtype out) {
-    if (in == SP24_E4M3)
+    if (in == SP24_E4M3 || in == SP24_I8)
         return out == SP24_BF16 || out == SP24_F32;
     return out == SP24_F16 || out == SP24_BF16 || out == SP24_F32;
 }

@@ -8,17 +8,19 @@
 // values and positions once) follows section 3.5 of the 2:4-versus-
 // quantization paper.
 //
-// Magnitude is compared on integer keys: the sign-stripped bit pattern, made
-// unique by appending (3 - position) as two low bits, so "larger key" means
+// Magnitude is compared on integer keys: the sign-stripped bit pattern (for
+// the sign-magnitude float formats) or |x| (for two's complement int8, so
+// -128 ranks above 127), made unique by appending (3 - position) as two low
+// bits, so "larger key" means
 // "larger magnitude, or equal magnitude at a lower position".  The kept pair
 // is then the largest and second-largest of four distinct integers.
 //
 // Work unit of the fast kernels: 16 bytes of dense input (8 x 16-bit or 16 x
-// fp8 elements = 2 or 4 groups) -> 8 bytes of values + 1 or 2 bytes of
+// 8-bit elements = 2 or 4 groups) -> 8 bytes of values + 1 or 2 bytes of
 // metadata.  Lanes of a wave take consecutive units, so every load is one
 // contiguous 1 KiB per wave instruction and every store is contiguous too.
 // HBM traffic per dense element: 2 + 1 + 0.125 = 3.125 B (16-bit) or
-// 1 + 0.5 + 0.125 = 1.625 B (fp8).
+// 1 + 0.5 + 0.125 = 1.625 B (fp8, int8).
 #include "sp24_internal.h"
 
 namespace sp24 {
@@ -55,18 +57,27 @@ __device__ __forceinline__ uint32_t group16(uint32_t e0, uint32_t e1, uint32_t e
     return pick(p0, e0, e1, e2, e3) | (pick(p1, e0, e1, e2, e3) << 16);
 }
 
-// One group of fp8 elements: returns the packed pair (v0 | v1 << 8).
+// Magnitude key of one byte: fp8 (sign-magnitude) or int8 (two's complement).
+template <bool INT8>
+__device__ __forceinline__ uint32_t mag8(uint32_t e) {
+    if (INT8)
+        return e & 0x80u ? 256u - e : e;    // |x|, 0 .. 128
+    return e & 0x7fu;
+}
+
+// One group of 8-bit elements: returns the packed pair (v0 | v1 << 8).
+template <bool INT8>
 __device__ __forceinline__ uint32_t group8(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3,
                                            uint32_t& nib) {
     uint32_t p0, p1;
-    top2(e0 & 0x7fu, e1 & 0x7fu, e2 & 0x7fu, e3 & 0x7fu, p0, p1);
+    top2(mag8<INT8>(e0), mag8<INT8>(e1), mag8<INT8>(e2), mag8<INT8>(e3), p0, p1);
     nib = p0 | (p1 << 2);
     return pick(p0, e0, e1, e2, e3) | (pick(p1, e0, e1, e2, e3) << 8);
 }
 
 // ---------------------------------------------------------------- fast path
 // Requires K*eb % 16 == 0, 16-byte aligned src rows, 8-byte aligned values.
-template <int EB>
+template <int EB, bool INT8>
 __global__ void __launch_bounds__(kThreads)
 prune_compress_units(const uint8_t* __restrict__ src, int64_t ld_bytes, uint32_t units_per_row,
                      uint32_t total_units, uint8_t* __restrict__ values, int64_t vrow_bytes,
@@ -99,7 +110,7 @@ prune_compress_units(const uint8_t* __restrict__ src, int64_t ld_bytes, uint32_t
             uint32_t n[4], pr[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                pr[g] = group8(w[g] & 0xffu, (w[g] >> 8) & 0xffu, (w[g] >> 16) & 0xffu, w[g] >> 24, n[g]);
+                pr[g] = group8<INT8>(w[g] & 0xffu, (w[g] >> 8) & 0xffu, (w[g] >> 16) & 0xffu, w[g] >> 24, n[g]);
             out.x = pr[0] | (pr[1] << 16);
             out.y = pr[2] | (pr[3] << 16);
             *reinterpret_cast<uint16_t*>(mrow + 2 * col[j]) =
@@ -166,7 +177,7 @@ decompress_units(const uint8_t* __restrict__ values, int64_t vrow_bytes,
 // ---------------------------------------------------------------- general path
 // Any K % 4 == 0, any strides and alignments: one thread per metadata word
 // (up to 8 groups), element-wise loads and stores.
-template <int EB>
+template <int EB, bool INT8>
 __global__ void __launch_bounds__(kThreads)
 prune_compress_words(const uint8_t* __restrict__ src, int64_t ld, int64_t rows, int64_t K,
                      uint8_t* __restrict__ values, uint32_t* __restrict__ meta) {
@@ -187,7 +198,7 @@ prune_compress_words(const uint8_t* __restrict__ src, int64_t ld, int64_t rows, 
             e[i] = EB == 2 ? (uint32_t)p[0] | ((uint32_t)p[1] << 8) : (uint32_t)p[0];
         }
         uint32_t nib, pr;
-        pr = EB == 2 ? group16(e[0], e[1], e[2], e[3], nib) : group8(e[0], e[1], e[2], e[3], nib);
+        pr = EB == 2 ? group16(e[0], e[1], e[2], e[3], nib) : group8<INT8>(e[0], e[1], e[2], e[3], nib);
         uint8_t* v = values + (r * (K / 2) + 2 * g) * EB;
         for (int b = 0; b < 2 * EB; ++b)
             v[b] = (uint8_t)(pr >> (8 * b));
@@ -238,14 +249,16 @@ hipError_t launch_prune_compress(sp24_dtype dt, int64_t rows, int64_t K, const v
     if (fast) {
         uint32_t upr = (uint32_t)(row_bytes / 16);
         uint32_t blocks = (uint32_t)((units + kThreads * kUnitsPerThread - 1) / (kThreads * kUnitsPerThread));
-        auto kern = eb == 2 ? prune_compress_units<2> : prune_compress_units<1>;
+        auto kern = eb == 2 ? prune_compress_units<2, false>
+                            : (dt == SP24_I8 ? prune_compress_units<1, true> : prune_compress_units<1, false>);
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, s, (const uint8_t*)src, ld_src * eb,
                            upr, (uint32_t)units, (uint8_t*)values, row_bytes / 2, (uint8_t*)meta,
                            meta_words(K) * 4, (uint32_t)(K / 8));
     } else {
         int64_t threads = rows * meta_words(K);
         uint32_t blocks = (uint32_t)((threads + kThreads - 1) / kThreads);
-        auto kern = eb == 2 ? prune_compress_words<2> : prune_compress_words<1>;
+        auto kern = eb == 2 ? prune_compress_words<2, false>
+                            : (dt == SP24_I8 ? prune_compress_words<1, true> : prune_compress_words<1, false>);
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, s, (const uint8_t*)src, ld_src, rows,
                            K, (uint8_t*)values, meta);
     }

@@ -45,45 +45,27 @@ struct DenseOp16<SP24_F16> {
                                                       __builtin_bit_cast(f16x8, b1), c, 0, 0, 0);
     }
 };
+// int8: two v_mfma_i32_16x16x64_i8 per 128-K step (lane l: row l%16, 16
+// bytes of K at 16*(l/16) of each half); int32 accumulation in the
+// accumulator registers' bits, converted after the K loop.
+template <>
+struct DenseOp16<SP24_I8> {
+    static constexpr int KSTEP = 128, ELEM = 1;
+    __device__ static __forceinline__ f32x4 mma(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x4 c) {
+        i32x4 ci = __builtin_bit_cast(i32x4, c);
+        ci = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a0), __builtin_bit_cast(i32x4, b0),
+                                                   ci, 0, 0, 0);
+        ci = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a1), __builtin_bit_cast(i32x4, b1),
+                                                   ci, 0, 0, 0);
+        return __builtin_bit_cast(f32x4, ci);
+    }
+};
 template <>
 struct DenseOp16<SP24_E4M3> {
     static constexpr int KSTEP = 128, ELEM = 1;
     __device__ static __forceinline__ f32x4 mma(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x4 c) {
         struct { uint4 x, y; } aa = {a0, a1}, bb = {b0, b1};
         return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            __builtin_bit_cast(i32x8, aa), __builtin_bit_cast(i32x8, bb), c, 0, 0, 0, 0x7f, 0, 0x7f);
-    }
-};
-
-// 32x32 output fragment over one 16-byte-per-lane K slice (16-bit: 16 K
-// with 8 per lane; fp8: 64 K with 32 bytes per lane = two slices).
-template <sp24_dtype DT>
-struct DenseOp32;
-template <>
-struct DenseOp32<SP24_BF16> {
-    static constexpr int KSTEP = 64, ELEM = 2, SUB = 4;   // 4 instructions per 64-K step
-    static constexpr int SUB_BYTES = 32;                  // bytes of K per instruction per row
-    __device__ static __forceinline__ f32x16 mma(uint4 a0, uint4, uint4 b0, uint4, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
-                                                       __builtin_bit_cast(bf16x8, b0), c, 0, 0, 0);
-    }
-};
-template <>
-struct DenseOp32<SP24_F16> {
-    static constexpr int KSTEP = 64, ELEM = 2, SUB = 4;
-    static constexpr int SUB_BYTES = 32;
-    __device__ static __forceinline__ f32x16 mma(uint4 a0, uint4, uint4 b0, uint4, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a0),
-                                                      __builtin_bit_cast(f16x8, b0), c, 0, 0, 0);
-    }
-};
-template <>
-struct DenseOp32<SP24_E4M3> {
-    static constexpr int KSTEP = 128, ELEM = 1, SUB = 2;  // 2 instructions per 128-K step
-    static constexpr int SUB_BYTES = 64;
-    __device__ static __forceinline__ f32x16 mma(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x16 c) {
-        struct { uint4 x, y; } aa = {a0, a1}, bb = {b0, b1};
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             __builtin_bit_cast(i32x8, aa), __builtin_bit_cast(i32x8, bb), c, 0, 0, 0, 0x7f, 0, 0x7f);
     }
 };
@@ -160,8 +142,16 @@ dense_skinny(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const
         const int al = o & 15, bl = o >> 4;
         const int mt = bl >> 4, ln = ((al >> 2) << 4) | (bl & 15), i = al & 3;
         float v = 0.f;
-        for (int w = 0; w < WAVES; ++w)   // fixed order: deterministic
-            v += red[w][mt][i][ln];
+        if constexpr (DT == SP24_I8) {
+            // int32 partial sums (their bits in red): added exactly, converted once
+            int vi = 0;
+            for (int w = 0; w < WAVES; ++w)
+                vi += __builtin_bit_cast(int, red[w][mt][i][ln]);
+            v = (float)vi;
+        } else {
+            for (int w = 0; w < WAVES; ++w)   // fixed order: deterministic
+                v += red[w][mt][i][ln];
+        }
         const int n = n0 + al, m = bl;
         if (n < N && m < M) {
             if (sx)
@@ -221,6 +211,9 @@ hipError_t launch_dense_gemm(const DenseArgs& g, hipStream_t s, const char** kna
     case SP24_E4M3:
         if (g.out_dt == SP24_BF16) return dispatch<SP24_E4M3, SP24_BF16>(g, s, kname);
         return dispatch<SP24_E4M3, SP24_F32>(g, s, kname);
+    case SP24_I8:
+        if (g.out_dt == SP24_BF16) return dispatch<SP24_I8, SP24_BF16>(g, s, kname);
+        return dispatch<SP24_I8, SP24_F32>(g, s, kname);
     default:
         return hipErrorInvalidValue;
     }

@@ -59,6 +59,17 @@ struct Dense32<SP24_F16> {
                                                       __builtin_bit_cast(f16x8, b[0]), c, 0, 0, 0);
     }
 };
+// int8: 32 K (32 bytes per row) per instruction, int32 accumulation in the
+// accumulator registers' bits, converted in the epilogue.
+template <>
+struct Dense32<SP24_I8> {
+    static constexpr int KSTEP = 128, SUB = 4, CHUNKS = 1;
+    __device__ static __forceinline__ f32x16 mma(const uint4* a, const uint4* b, f32x16 c) {
+        typedef __attribute__((ext_vector_type(16))) int i32x16;
+        return __builtin_bit_cast(f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+            __builtin_bit_cast(i32x4, a[0]), __builtin_bit_cast(i32x4, b[0]), __builtin_bit_cast(i32x16, c), 0, 0, 0));
+    }
+};
 template <>
 struct Dense32<SP24_E4M3> {
     static constexpr int KSTEP = 128, SUB = 2, CHUNKS = 2;  // 32 B per lane per instruction
@@ -98,7 +109,7 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
     const int ta = group * G + within % g_rows, tb = within / g_rows;
     const int a0 = ta * kBA, b0 = tb * kBB;
 
-    const uint32_t row_bytes = (uint32_t)K * (DT == SP24_E4M3 ? 1 : 2);
+    const uint32_t row_bytes = (uint32_t)K * (DT == SP24_E4M3 || DT == SP24_I8 ? 1 : 2);
     const int steps = (int)((row_bytes + 127) / 128);   // the last may be partial
     const Buf bufW(W, (uint32_t)N * row_bytes);           // rows past N / M read as zeros
     const Buf bufX(X, (uint32_t)M * row_bytes);
@@ -197,6 +208,7 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
             if (m >= M)
                 continue;
             const float fsx = sx ? sx[m] : 1.f;
+            const f32x16 accf = acc_to_f32<DT>(acc[i][j]);
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 const int n = a0 + wa * 32 * kFA + i * 32 + 8 * h + 4 * kg;
@@ -205,7 +217,7 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
                 f32x4 v;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    v[q] = acc[i][j][4 * h + q] * fsx * (sw && n + q < N ? sw[n + q] : 1.f);
+                    v[q] = accf[4 * h + q] * fsx * (sw && n + q < N ? sw[n + q] : 1.f);
                 const int64_t off = (int64_t)m * N + n;
                 if (n + 3 < N && (off & 3) == 0) {
                     store_out4<OUT>(Y, off, v);
@@ -268,6 +280,9 @@ hipError_t launch_dense_gemm_big(const DenseArgs& g, hipStream_t s, const char**
     case SP24_E4M3:
         if (g.out_dt == SP24_BF16) return launch<SP24_E4M3, SP24_BF16>(g, s, kname);
         return launch<SP24_E4M3, SP24_F32>(g, s, kname);
+    case SP24_I8:
+        if (g.out_dt == SP24_BF16) return launch<SP24_I8, SP24_BF16>(g, s, kname);
+        return launch<SP24_I8, SP24_F32>(g, s, kname);
     default:
         return hipErrorInvalidValue;
     }

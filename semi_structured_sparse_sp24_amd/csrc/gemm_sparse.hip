@@ -206,8 +206,16 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
         const int al = ot & 15, bl = ot >> 4;
         const int mt = bl >> 4, ln = ((al >> 2) << 4) | (bl & 15), i = al & 3;
         float v = 0.f;
-        for (int w = 0; w < WAVES; ++w)   // fixed order: deterministic
-            v += red[w][t][mt][i][ln];
+        if constexpr (DT == SP24_I8) {
+            // int32 partial sums (their bits in red): added exactly, converted once
+            int vi = 0;
+            for (int w = 0; w < WAVES; ++w)
+                vi += __builtin_bit_cast(int, red[w][t][mt][i][ln]);
+            v = (float)vi;
+        } else {
+            for (int w = 0; w < WAVES; ++w)   // fixed order: deterministic
+                v += red[w][t][mt][i][ln];
+        }
         const int ar = a0 + 16 * t + al, br = bl;
         if (ar < RA && br < RB) {
             if (sa)
@@ -288,6 +296,9 @@ hipError_t launch_sp24_gemm(const GemmArgs& g, hipStream_t s, const char** kname
     case SP24_E4M3:
         if (g.out_dt == SP24_BF16) return dispatch<SP24_E4M3, SP24_BF16>(g, s, kname);
         return dispatch<SP24_E4M3, SP24_F32>(g, s, kname);
+    case SP24_I8:
+        if (g.out_dt == SP24_BF16) return dispatch<SP24_I8, SP24_BF16>(g, s, kname);
+        return dispatch<SP24_I8, SP24_F32>(g, s, kname);
     default:
         return hipErrorInvalidValue;
     }

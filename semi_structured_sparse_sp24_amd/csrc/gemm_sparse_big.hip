@@ -80,7 +80,7 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // lo gets the values at positions 0, 1 of every group, hi those at 2, 3.
 template <sp24_dtype DT>
 __device__ __forceinline__ void split_halves(const uint4& q0, const uint4& q1, uint4& lo, uint4& hi) {
-    if constexpr (DT == SP24_E4M3) {
+    if constexpr (SparseOp<DT>::ELEM == 1) {
         // a group is one dword: bytes 0, 1 and bytes 2, 3
         lo = make_uint4(__builtin_amdgcn_perm(q0.y, q0.x, 0x05040100u), __builtin_amdgcn_perm(q0.w, q0.z, 0x05040100u),
                         __builtin_amdgcn_perm(q1.y, q1.x, 0x05040100u), __builtin_amdgcn_perm(q1.w, q1.z, 0x05040100u));
@@ -304,7 +304,7 @@ __device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a
             const int br = b0 + wb * 16 * kFB + j * 16 + r;
             if (br >= RB || ar >= RA)
                 continue;
-            f32x4 v = acc[i][j];
+            f32x4 v = acc_to_f32<DT>(acc[i][j]);
             const float fsb = sb ? sb[br] : 1.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -470,6 +470,9 @@ hipError_t launch_sp24_gemm_big(const GemmArgs& g, hipStream_t s, const char** k
     case SP24_E4M3:
         if (g.out_dt == SP24_BF16) return launch_big<SP24_E4M3, SP24_BF16>(g, s, kname);
         return launch_big<SP24_E4M3, SP24_F32>(g, s, kname);
+    case SP24_I8:
+        if (g.out_dt == SP24_BF16) return launch_big<SP24_I8, SP24_BF16>(g, s, kname);
+        return launch_big<SP24_I8, SP24_F32>(g, s, kname);
     default:
         return hipErrorInvalidValue;
     }
@@ -488,6 +491,9 @@ hipError_t launch_sp24_hybrid(const HybridArgs& h, hipStream_t s, const char** k
     case SP24_E4M3:
         if (h.out_dt == SP24_BF16) return launch_hybrid<SP24_E4M3, SP24_BF16>(h, s, kname);
         return launch_hybrid<SP24_E4M3, SP24_F32>(h, s, kname);
+    case SP24_I8:
+        if (h.out_dt == SP24_BF16) return launch_hybrid<SP24_I8, SP24_BF16>(h, s, kname);
+        return launch_hybrid<SP24_I8, SP24_F32>(h, s, kname);
     default:
         return hipErrorInvalidValue;
     }

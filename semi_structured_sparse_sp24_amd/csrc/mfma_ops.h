@@ -14,7 +14,7 @@
 //     B, lane l: column l%16; 16 values = dense K [8*(l/16), +8) followed by
 //        dense K [32 + 8*(l/16), +8);
 //     D, lane l: D[4*(l/16) + i][l%16], i = 0..3.
-//   v_smfmac_f32_16x16x128_fp8_fp8      (one step = 128 dense K)
+//   v_smfmac_f32_16x16x128_fp8_fp8, v_smfmac_i32_16x16x128_i8  (one step = 128 dense K)
 //     A, lane l: row l%16; 16 compressed bytes = the 8 groups of dense K
 //        [32*(l/16), +32); index: all 32 bits, group j's nibble at [4j, 4j+3];
 //     B, lane l: column l%16; 32 bytes = dense K [16*(l/16), +16) then
@@ -94,6 +94,38 @@ struct SparseOp<SP24_E4M3> {
         return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(av, bv, c, (int)idx, 0, 0);
     }
 };
+
+// The int8 form: the same operand layout as fp8, int32 accumulation.  The
+// accumulator registers hold the int32 bits (exact: at most K * 128 * 127 in
+// magnitude); acc_to_f32 converts them once, after the K loop.
+template <>
+struct SparseOp<SP24_I8> {
+    static constexpr int KSTEP = 128;
+    static constexpr int ELEM = 1;
+    __device__ static __forceinline__ f32x4 mma(uint4 a, uint4 b0, uint4 b1, uint32_t idx, f32x4 c) {
+        i32x4 av = __builtin_bit_cast(i32x4, a);
+        struct { uint4 x, y; } bb = {b0, b1};
+        i32x8 bv = __builtin_bit_cast(i32x8, bb);
+        i32x4 ci = __builtin_bit_cast(i32x4, c);
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_smfmac_i32_16x16x128_i8(av, bv, ci, (int)idx, 0, 0));
+    }
+};
+
+// Accumulators as fp32 values: int8 accumulates int32 bits in the same
+// registers, every other input dtype fp32 already.
+template <sp24_dtype DT>
+__device__ __forceinline__ f32x4 acc_to_f32(f32x4 v) {
+    if constexpr (DT == SP24_I8)
+        return __builtin_convertvector(__builtin_bit_cast(i32x4, v), f32x4);
+    return v;
+}
+template <sp24_dtype DT>
+__device__ __forceinline__ f32x16 acc_to_f32(f32x16 v) {
+    typedef __attribute__((ext_vector_type(16))) int i32x16;
+    if constexpr (DT == SP24_I8)
+        return __builtin_convertvector(__builtin_bit_cast(i32x16, v), f32x16);
+    return v;
+}
 
 // Byte offsets, within one step of one row, of what lane group kg loads.
 //   A values: 16 bytes at a_off(kg) of the row's compressed step (KSTEP/2 values)

@@ -19,12 +19,12 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
-inline int elem_bytes(sp24_dtype dt) { return dt == SP24_E4M3 ? 1 : (dt == SP24_F32 ? 4 : 2); }
+inline int elem_bytes(sp24_dtype dt) { return dt == SP24_E4M3 || dt == SP24_I8 ? 1 : (dt == SP24_F32 ? 4 : 2); }
 inline int64_t meta_words(int64_t K) { return (K + 31) / 32; }
 
 // K consumed by one sparse MFMA step, per input dtype: 64 for 16-bit
 // (v_smfmac_*_16x16x64), 128 for fp8 (v_smfmac_*_16x16x128).
-inline int64_t gemm_k_tile(sp24_dtype dt) { return dt == SP24_E4M3 ? 128 : 64; }
+inline int64_t gemm_k_tile(sp24_dtype dt) { return elem_bytes(dt) == 1 ? 128 : 64; }
 
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error; arguments were validated by

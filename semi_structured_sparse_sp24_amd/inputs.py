@@ -31,13 +31,14 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-F16, BF16, E4M3, F32 = 0, 1, 2, 3
+F16, BF16, E4M3, F32, I8 = 0, 1, 2, 3, 4
 FP8_MAX = 448.0
+I8_MAX = 127.0
 
 TORCH_DTYPE = {F16: torch.float16, BF16: torch.bfloat16, E4M3: torch.float8_e4m3fn,
-               F32: torch.float32}
-BITS_DTYPE = {F16: np.uint16, BF16: np.uint16, E4M3: np.uint8, F32: np.uint32}
-ELEM_BYTES = {F16: 2, BF16: 2, E4M3: 1, F32: 4}
+               F32: torch.float32, I8: torch.int8}
+BITS_DTYPE = {F16: np.uint16, BF16: np.uint16, E4M3: np.uint8, F32: np.uint32, I8: np.uint8}
+ELEM_BYTES = {F16: 2, BF16: 2, E4M3: 1, F32: 4, I8: 1}
 
 WORKLOADS = {
     "tiny": dict(index=1, dtype=F16, out=F16, shapes=[(256, 256)], ms=[16]),
@@ -52,6 +53,9 @@ WORKLOADS = {
     "online": dict(index=5, dtype=BF16, out=BF16, shapes=[(4096, 4096)], ms=[4096]),
     "online_fp8": dict(index=6, dtype=E4M3, act=BF16, out=BF16, shapes=[(4096, 4096), (28672, 4096)],
                        ms=[4096]),
+    # the fp8 shapes in symmetric per-row int8 (the 2:4 + INT8 variant)
+    "int8": dict(index=8, dtype=I8, out=BF16,
+                 shapes=[(5120, 5120), (51200, 5120), (5120, 25600)], ms=[1, 64, 4096]),
     # the prefill layers with one output row in eight kept dense (hybrid_split)
     "hybrid": dict(index=7, dtype=BF16, out=BF16,
                    shapes=[(4096, 4096), (6144, 4096), (28672, 4096), (4096, 14336)], ms=[2048, 8192]),
@@ -90,6 +94,16 @@ def quantize_e4m3_rows(t: torch.Tensor):
     return to_bits(q, E4M3), scale.numpy().astype(np.float32)
 
 
+def quantize_i8_rows(t: torch.Tensor):
+    """Symmetric int8 with one fp32 scale per row (absmax / 127; 1 for an
+    all-zero row): round half to even, clamp to +-127.  Returns (bits as
+    uint8, scales)."""
+    absmax = t.abs().amax(dim=1)
+    scale = torch.where(absmax > 0, absmax / I8_MAX, torch.ones_like(absmax)).to(torch.float32)
+    q = torch.round(t / scale[:, None]).clamp(-I8_MAX, I8_MAX).to(torch.int8)
+    return q.numpy().view(np.uint8).copy(), scale.numpy().astype(np.float32)
+
+
 def outliers(t: torch.Tensor, frac: float, factor: float, seed: int) -> torch.Tensor:
     g = torch.Generator("cpu").manual_seed(int(seed))
     mask = torch.rand(*t.shape, generator=g) < frac
@@ -103,6 +117,8 @@ def weight(workload: str, s: int):
     t = normal((N, K), 0.02, seed_of(w["index"], s, 0, 0))
     if w["dtype"] == E4M3:
         return quantize_e4m3_rows(t)
+    if w["dtype"] == I8:
+        return quantize_i8_rows(t)
     return to_bits(t, w["dtype"]), None
 
 
@@ -118,6 +134,8 @@ def activation(workload: str, s: int, j: int, M: int | None = None):
     act = w.get("act", w["dtype"])
     if act == E4M3:
         return quantize_e4m3_rows(t)
+    if act == I8:
+        return quantize_i8_rows(t)
     return to_bits(t, act), None
 
 

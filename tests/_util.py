@@ -8,16 +8,19 @@ import torch
 import oracle
 
 TORCH_OF = {oracle.F16: torch.float16, oracle.BF16: torch.bfloat16, oracle.E4M3: torch.float8_e4m3fn,
-            oracle.F32: torch.float32}
-VIEW_OF = {oracle.F16: torch.int16, oracle.BF16: torch.int16, oracle.E4M3: torch.uint8, oracle.F32: torch.int32}
-NP_OF = {oracle.F16: np.uint16, oracle.BF16: np.uint16, oracle.E4M3: np.uint8, oracle.F32: np.uint32}
+            oracle.F32: torch.float32, oracle.I8: torch.int8}
+VIEW_OF = {oracle.F16: torch.int16, oracle.BF16: torch.int16, oracle.E4M3: torch.uint8, oracle.F32: torch.int32,
+           oracle.I8: torch.uint8}
+NP_OF = {oracle.F16: np.uint16, oracle.BF16: np.uint16, oracle.E4M3: np.uint8, oracle.F32: np.uint32,
+         oracle.I8: np.uint8}
 
 # Parity bar for GEMM outputs: max |Y - R| / max(|R|, rms R).  fp16/bf16 inputs
 # with fp32 accumulation: 1e-2; fp8 e4m3: 3e-2 (both sides on the same
-# e4m3-decoded values).  The error the arithmetic itself allows is far lower:
+# e4m3-decoded values); int8: 1e-2 (exact int32 sums, one conversion and
+# the output rounding).  The error the arithmetic itself allows is far lower:
 # one output rounding (bf16: 2^-9 relative) plus fp32 accumulation
 # (~sqrt(K) * 2^-24 relative to sum |x w|).
-TOL = {oracle.F16: 1e-2, oracle.BF16: 1e-2, oracle.E4M3: 3e-2}
+TOL = {oracle.F16: 1e-2, oracle.BF16: 1e-2, oracle.E4M3: 3e-2, oracle.I8: 1e-2}
 
 
 def say(*msg):

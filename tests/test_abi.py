@@ -264,3 +264,18 @@ def test_hybrid_validation_precedes_hip():
     assert k(bf, bf, 512, 512, 256, 4096) == "sp24_hybrid_128x128"
     assert k(bf, bf, 0, 16, 8, 64) == "none" and k(bf, bf, 4, 16, 8, 0) == "fill_zero"
     assert k(bf, bf, 4, 12, 8, 64) is None and k(bf, bf, 4, 16, 8, 96) is None
+
+
+def test_int8_dtype_rules():
+    f = sp.lib().sp24_gemm
+    # int8 needs whole 128-K steps and an fp32 / bf16 output; dtype codes past int8 are rejected
+    assert f(0, sp.I8, sp.BF16, 4, 16, 64, 16, 32, 48, None, None, 80, None) == 4
+    assert f(0, sp.I8, sp.F16, 4, 16, 128, 16, 32, 48, None, None, 80, None) == 3
+    assert f(0, 5, sp.BF16, 4, 16, 128, 16, 32, 48, None, None, 80, None) == 3
+    i8, bf = __import__("torch").int8, __import__("torch").bfloat16
+    assert sp.gemm_kernel(True, sp.SPARSE_W, i8, bf, 1, 4096, 4096) == "sp24_skinny_x4"
+    assert sp.gemm_kernel(True, sp.SPARSE_W, i8, bf, 4096, 4096, 4096) == "sp24_big_256x256"
+    assert sp.gemm_kernel(False, sp.SPARSE_W, i8, bf, 4096, 4096, 4096) == "dense_big_256x256"
+    assert sp.gemm_kernel(True, sp.SPARSE_W, i8, bf, 4, 4096, 64) is None
+    # prune+compress accepts int8 (any alignment, a general kernel takes the rest)
+    assert sp.lib().sp24_prune_compress(sp.I8, 0, 64, None, 64, None, None, None) == 0

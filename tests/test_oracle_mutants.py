@@ -10,6 +10,7 @@ import oracle
 from tests import test_oracle_audit as audit
 from tests import test_oracle_codecs as codecs
 from tests import test_oracle_gemm as gemm
+from tests import test_oracle_int8 as int8
 from tests import test_oracle_prune as prune
 from tests import test_oracle_quant as quant
 
@@ -39,6 +40,8 @@ MUTANTS = [
     ("audit-fallback-skips-ineligible", "n_dense += 1;", "n_dense += eligible[i] ? 1 : 0;"),
     ("audit-selection-over-candidates", "(double)n_sparse / (double)n_eligible", "(double)n_sparse / (double)candidate"),
     ("audit-ignores-eligibility", "if (eligible[i] && sparse[i]) {", "if (sparse[i]) {"),
+    ("int8-magnitude-from-bits", "    if (dt == OR_I8) {\n        int v", "    if (0) {\n        int v"),
+    ("int8-decoded-unsigned", "return (double)((const int8_t *)base)[i];", "return (double)((const uint8_t *)base)[i];"),
 ]
 
 PINS = [
@@ -62,6 +65,9 @@ PINS = [
     audit.test_coverage_worked_by_hand,
     audit.test_invariants,
     audit.test_extremes,
+    int8.test_decode_every_int8_pattern,
+    int8.test_prune_matches_brute_force_and_orders_minus_128_first,
+    int8.test_int8_gemm_is_exact_integer_arithmetic,
 ]
 
 
