@@ -18,9 +18,9 @@
 //     accumulators between register files inside the loop; two waves per
 //     SIMD also hide each other's LDS latency.)
 //   - K advances one instruction step per stage: A 256 rows x 64 B and B 256
-//     rows x 128 B; metadata comes in blocks of 16 B per row (two 16-bit
-//     steps, or one fp8 step); three stages and three metadata blocks live in
-//     LDS (156 KB of the 160 KB);
+//     rows x 128 B; metadata comes in blocks of 32 B per row (four 16-bit
+//     steps, or two fp8 steps); three stages and two metadata blocks fill
+//     the 160 KB of LDS;
 //   - the stages are filled by direct global->LDS loads (buffer_load_dwordx4
 //     ... lds): no registers, no LDS write instructions; two steps are in
 //     flight while the third is consumed, with one barrier per step;
@@ -38,6 +38,10 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Metadata in LDS: blocks of kMetaRow bytes per A row (four 16-bit steps, or
+// two fp8 steps), in a ring of kMetaSlots blocks.
+constexpr int kMetaRow = 32, kMetaSlots = 2;
+
 // Tile shapes: BA rows of A x BB rows of B, WA x WB waves, OCC workgroups per CU.
 template <int BA_, int BB_, int WA_, int WB_, int OCC_>
 struct Tile {
@@ -46,7 +50,7 @@ struct Tile {
     static constexpr int FA = BA / 16 / WA, FB = BB / 16 / WB;   // 16x16 fragments per wave
     static constexpr int A_STAGE = BA * 64;    // bytes of compressed A per stage
     static constexpr int B_STAGE = BB * 128;   // bytes of dense B per stage
-    static constexpr int M_BLOCK = BA * 16;    // bytes of one metadata block
+    static constexpr int M_BLOCK = BA * kMetaRow;   // bytes of one metadata block
 };
 using T256x256 = Tile<256, 256, 2, 4, 1>;
 using T256x128 = Tile<256, 128, 4, 2, 1>;
@@ -102,8 +106,7 @@ __device__ __forceinline__ void split_halves(const uint4& q0, const uint4& q1, u
 // Y, sa and RA refer to this tile's region of A rows; `group` is the tile's
 // group of tile-sharing workgroups (it sets the K rotation).
 template <sp24_dtype DT, sp24_dtype OUT, class TL, bool DENSE>
-__device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a2s, uint8_t* b0s, uint8_t* b1s,
-                                          uint8_t* b2s, uint8_t* m0s, uint8_t* m1s, uint8_t* m2s,
+__device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* msb,
                                           const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
                                           const uint8_t* __restrict__ B, const float* __restrict__ sa,
                                           const float* __restrict__ sb, void* __restrict__ Y, int RA, int RB,
@@ -111,10 +114,15 @@ __device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a
     using L = StepLayout<DT>;
     using Op = SparseOp<DT>;
     constexpr int MWS = L::META_WORDS;                  // metadata words per row per step: 2 or 4
-    // metadata goes in blocks of 16 bytes per row: T steps (2 for 16-bit, 1
-    // for fp8), one 16-byte load per row -- a request per row per block where
-    // per-step 4-byte loads cost a request per row per step
-    constexpr int T = 4 / MWS;
+    // metadata goes in blocks of kMetaRow bytes per row: T steps (4 for
+    // 16-bit, 2 for fp8).  Each row of a block is one request to L2, which
+    // costs about as much as a full line of A or B: the fewer blocks, the
+    // fewer requests (per-step 4-byte loads cost one per row and step).
+    constexpr int T = kMetaRow / (4 * MWS);
+    // a block slot is reloaded T * kMetaSlots steps after its previous load,
+    // which must be at least 3 (the steps in flight) for its last reader to
+    // have passed the barrier that precedes the reload
+    static_assert(T * kMetaSlots >= 3, "metadata ring too short");
     constexpr int kBA = DENSE ? TL::BA / 2 : TL::BA;    // A rows of this tile
     constexpr int kBB = TL::BB, kWB = TL::WB, kWaves = TL::WAVES, kFB = TL::FB;
     constexpr int kFA = kBA / 16 / TL::WA;
@@ -131,7 +139,7 @@ __device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a
     constexpr int A_CH = A_ROW_STEP / 16;               // 16-byte chunks per row step: 4, or 8 dense
     constexpr bool META = !DENSE;
     constexpr int AB = A_LOADS + B_LOADS;
-    constexpr int U = 3 * T;                            // loop unroll: a whole number of stages and blocks
+    constexpr int U = T;                                // loop unroll: one metadata block
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -161,8 +169,15 @@ __device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         gb[j] = (uint32_t)(b0 + row) * b_row_bytes + 16 * c;
     }
-    // metadata: wave w < M_WAVES loads rows [64 w, 64 w + 64), 16 bytes each
-    const uint32_t gm = (uint32_t)(a0 + 64 * min(wave, M_WAVES - 1) + lane) * m_row_bytes;
+    // metadata: wave w < M_WAVES loads M_RPL rows of a block, M_CPR chunks of
+    // 16 bytes each; in LDS the two chunks of a row trade places on every
+    // other group of 8 rows, so that the 16 rows a fragment reads fall in 16
+    // different 16-byte bank groups
+    constexpr int M_CPR = kMetaRow / 16, M_RPL = 1024 / kMetaRow;
+    static_assert(M_CPR == 1 || M_CPR == 2, "metadata chunks per row");
+    auto m_swz = [](int row) { return M_CPR == 2 ? (row >> 3) & 1 : 0; };
+    const int m_ld_row = M_RPL * min(wave, M_WAVES - 1) + lane / M_CPR;
+    const uint32_t gm = (uint32_t)(a0 + m_ld_row) * m_row_bytes + 16 * ((lane % M_CPR) ^ m_swz(m_ld_row));
 
     // K loop start rotated per group of tile-sharing workgroups: members of a
     // group (resident together on one XCD) walk K in step and share operand
@@ -186,8 +201,8 @@ __device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j)
                 dma16(bufB, bs + 1024 * (B_LOADS * wave + j), gb[j], sB);
-            // the block of steps s .. s + T - 1 (with T = 2 and an odd step count,
-            // the last block's second half is past the row: read, never used)
+            // the block of steps s .. s + T - 1 (with a step count that T does
+            // not divide, the last block's tail is past the row: read, never used)
             if (META && ms != nullptr && wave < M_WAVES)
                 dma16(bufM, ms + 1024 * wave, gm, live ? (uint32_t)s * (4 * MWS) : kOOB);
         }
@@ -208,7 +223,9 @@ __device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a
     // dense rows: the lane's 32 bytes are chunks 2 kg and 2 kg + 1 of its row
     const int a_frag_d0 = a_row * 128 + 16 * ((2 * kg) ^ ((r >> 1) & 7));
     const int a_frag_d1 = a_row * 128 + 16 * ((2 * kg + 1) ^ ((r >> 1) & 7));
-    const int m_frag = a_row * 16 + 4 * L::meta_word(kg);
+    // the lane's metadata word in chunk 0 or 1 of its row (before the step's offset)
+    const int m_frag0 = a_row * kMetaRow + 16 * (0 ^ m_swz(a_row)) + 4 * L::meta_word(kg);
+    const int m_frag1 = a_row * kMetaRow + 16 * (1 ^ m_swz(a_row)) + 4 * L::meta_word(kg);
     const int msh = L::meta_shift(kg);
     const int b_frag0 = (wb * 16 * kFB + r) * 128 + 16 * (kg ^ ((r >> 1) & 7));
     const int b_frag1 = (wb * 16 * kFB + r) * 128 + 16 * ((4 + kg) ^ ((r >> 1) & 7));
@@ -235,7 +252,9 @@ __device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a
                 split_halves<DT>(q0, q1, fa[i], fh[i]);
             } else {
                 fa[i] = *reinterpret_cast<const uint4*>(as + a_frag + i * 16 * 64);
-                fi[i] = *reinterpret_cast<const uint32_t*>(ms + m_frag + 4 * MWS * u + i * 16 * 16) >> msh;
+                // step u's words start at word MWS u of the row's block
+                const int mo = (((MWS * u) >> 2) ? m_frag1 : m_frag0) + 4 * ((MWS * u) & 3);
+                fi[i] = *reinterpret_cast<const uint32_t*>(ms + mo + i * 16 * kMetaRow) >> msh;
             }
         }
     };
@@ -271,26 +290,33 @@ __device__ __forceinline__ void tile_body(uint8_t* a0s, uint8_t* a1s, uint8_t* a
     // barrier per step.  Before each step a wave waits for its own loads of
     // that step and for its LDS reads of the previous one; the barrier makes
     // every wave's loads visible and frees the stage the new loads overwrite.
-    // Stage of step x: x % 3; metadata block of step x: (x / T) % 3, loaded
-    // with the stage of its first step.  The loop runs U = 3 T steps per
-    // iteration (padded steps read zeros) so that both indices are static and
-    // the body has no exits, which keeps the accumulators in registers.
-    uint8_t* const as_[3] = {a0s, a1s, a2s};
-    uint8_t* const bs_[3] = {b0s, b1s, b2s};
-    uint8_t* const ms_[3] = {m0s, m1s, m2s};
-    issue(as_[0], bs_[0], ms_[0], 0);
-    issue(as_[1], bs_[1], 1 % T ? nullptr : ms_[1 / T], 1);
+    // Stage of step x: x % 3; metadata slot of step x: (x / T) % kMetaSlots,
+    // loaded with the stage of its first step.  The stage and the slot are
+    // run-time offsets; the loop runs T steps per iteration (padded steps
+    // read zeros), so that where a block starts is static and the body has
+    // no exits, which keeps the accumulators in registers.
+    auto sa_ = [&](int st) { return asb + st * kAStage; };
+    auto sb_ = [&](int st) { return bsb + st * kBStage; };
+    auto ms_ = [&](int blk) { return msb + (blk % kMetaSlots) * kMBlock; };
+    issue(sa_(0), sb_(0), ms_(0), 0);
+    issue(sa_(1), sb_(1), 1 % T ? nullptr : ms_(1 / T), 1);
     const int stepsU = (steps + U - 1) / U * U;
+    int st = 0;   // stage of step s
     for (int s = 0; s < stepsU; s += U) {
+        const int blk = s / T;   // metadata block of steps s .. s + T - 1
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             wait_step((u + 1) % T == 0);
             __builtin_amdgcn_s_barrier();
             const int x2 = u + 2;   // issued now: position within the unrolled block
-            uint8_t* const nms = x2 % T ? nullptr : ms_[(x2 / T) % 3];
-            load_a(as_[u % 3], ms_[(u / T) % 3], u % T);
-            compute_step(bs_[u % 3], [&] { issue_part(as_[x2 % 3], bs_[x2 % 3], nms, s + x2, true, false); },
-                         [&] { issue_part(as_[x2 % 3], bs_[x2 % 3], nms, s + x2, false, true); });
+            const int st2 = st == 0 ? 2 : st - 1;   // (s + u + 2) % 3
+            uint8_t* const nms = x2 % T ? nullptr : ms_(blk + x2 / T);
+            uint8_t* const nas = sa_(st2);
+            uint8_t* const nbs = sb_(st2);
+            load_a(sa_(st), ms_(blk + u / T), u % T);
+            compute_step(sb_(st), [&] { issue_part(nas, nbs, nms, s + x2, true, false); },
+                         [&] { issue_part(nas, nbs, nms, s + x2, false, true); });
+            st = st == 2 ? 0 : st + 1;
         }
     }
     wait_vmcnt<0>();   // drain the (useless) loads of steps past the end
@@ -340,9 +366,9 @@ __device__ __forceinline__ TilePos tile_pos(int t, int tiles_a, int tiles_b) {
 }
 
 #define SP24_TILE_LDS(TL)                                                                                    \
-    __shared__ __attribute__((aligned(1024))) uint8_t a0s[TL::A_STAGE], a1s[TL::A_STAGE], a2s[TL::A_STAGE]; \
-    __shared__ __attribute__((aligned(1024))) uint8_t b0s[TL::B_STAGE], b1s[TL::B_STAGE], b2s[TL::B_STAGE]; \
-    __shared__ __attribute__((aligned(1024))) uint8_t m0s[TL::M_BLOCK], m1s[TL::M_BLOCK], m2s[TL::M_BLOCK]
+    __shared__ __attribute__((aligned(1024))) uint8_t asb[3 * TL::A_STAGE];                              \
+    __shared__ __attribute__((aligned(1024))) uint8_t bsb[3 * TL::B_STAGE];                              \
+    __shared__ __attribute__((aligned(1024))) uint8_t msb[kMetaSlots * TL::M_BLOCK]
 
 template <sp24_dtype DT, sp24_dtype OUT, class TL>
 __global__ void __launch_bounds__(TL::THREADS, TL::OCC)
@@ -351,7 +377,7 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
          int64_t K, int64_t sya, int64_t syb, int tiles_a, int tiles_b) {
     SP24_TILE_LDS(TL);
     const TilePos p = tile_pos(xcd_order(gridDim.x), tiles_a, tiles_b);
-    tile_body<DT, OUT, TL, false>(a0s, a1s, a2s, b0s, b1s, b2s, m0s, m1s, m2s, av, am, B, sa, sb, Y, RA, RB, K,
+    tile_body<DT, OUT, TL, false>(asb, bsb, msb, av, am, B, sa, sb, Y, RA, RB, K,
                                   sya, syb, p.ta * TL::BA, p.tb * TL::BB, p.group);
 }
 
@@ -369,11 +395,11 @@ sp24_hybrid(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, con
     const int t = xcd_order(gridDim.x);
     if (t < tiles_s * tiles_b) {
         const TilePos p = tile_pos(t, tiles_s, tiles_b);
-        tile_body<DT, OUT, TL, false>(a0s, a1s, a2s, b0s, b1s, b2s, m0s, m1s, m2s, av, am, B, sa, sb, Y, RS, RB, K,
+        tile_body<DT, OUT, TL, false>(asb, bsb, msb, av, am, B, sa, sb, Y, RS, RB, K,
                                       sya, syb, p.ta * TL::BA, p.tb * TL::BB, p.group);
     } else {
         const TilePos p = tile_pos(t - tiles_s * tiles_b, tiles_d, tiles_b);
-        tile_body<DT, OUT, TL, true>(a0s, a1s, a2s, b0s, b1s, b2s, m0s, m1s, m2s, ad, nullptr, B, sd, sb, Yd, RD,
+        tile_body<DT, OUT, TL, true>(asb, bsb, msb, ad, nullptr, B, sd, sb, Yd, RD,
                                      RB, K, sya, syb, p.ta * (TL::BA / 2), p.tb * TL::BB, p.group);
     }
 }
