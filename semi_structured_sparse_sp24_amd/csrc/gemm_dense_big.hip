@@ -80,34 +80,42 @@ struct Dense32<SP24_E4M3> {
     }
 };
 
+// Workgroup b of nwg -> its place in an XCD-aware order (consecutive places
+// run on one XCD), and place t -> (group, W tile, X tile) in groups of 8 W
+// tiles x all X tiles.
+__device__ __forceinline__ int dxcd_order(int b, int nwg) {
+    const int xcd = b & 7, local = b >> 3;
+    const int per_xcd = (nwg + 7) >> 3, full = nwg & 7 ? (nwg & 7) : 8;
+    return xcd < full ? xcd * per_xcd + local : full * per_xcd + (xcd - full) * (per_xcd - 1) + local;
+}
+struct DTilePos {
+    int group, ta, tb;
+};
+__device__ __forceinline__ DTilePos dtile_pos(int t, int tiles_a, int tiles_b) {
+    constexpr int G = 8;
+    const int group = t / (G * tiles_b), within = t - group * G * tiles_b;
+    const int g_rows = min(G, tiles_a - group * G);
+    return {group, group * G + within % g_rows, within / g_rows};
+}
+
+// One output tile: W rows [a0, a0 + TL::BA) x X rows [b0, b0 + TL::BB), over
+// the whole K, in two LDS stages per operand (a0s/a1s, b0s/b1s).
 template <sp24_dtype DT, sp24_dtype OUT, class TL>
-__global__ void __launch_bounds__(TL::THREADS, TL::OCC)
-dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
-          const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K, int tiles_a,
-          int tiles_b) {
+__device__ __forceinline__ void dense_tile(uint8_t* a0s, uint8_t* a1s, uint8_t* b0s, uint8_t* b1s,
+                                           const uint8_t* __restrict__ W, const uint8_t* __restrict__ X,
+                                           const float* __restrict__ sx, const float* __restrict__ sw,
+                                           void* __restrict__ Y, int N, int M, int64_t K, int a0, int b0,
+                                           int group) {
     using Op = Dense32<DT>;
     constexpr int kBA = TL::BA, kBB = TL::BB, kWB = TL::WB, kFA = TL::FA, kFB = TL::FB;
     constexpr int LA = TL::LA, LB = TL::LB;
     static_assert(LA * TL::WAVES * 1024 == kBA * 128 && LB * TL::WAVES * 1024 == kBB * 128, "whole loads");
     constexpr int LOADS = LA + LB;                  // per wave per stage
-    __shared__ __attribute__((aligned(1024))) uint8_t a0s[kBA * 128], a1s[kBA * 128];
-    __shared__ __attribute__((aligned(1024))) uint8_t b0s[kBB * 128], b1s[kBB * 128];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, kg = lane >> 5;
     const int wa = wave / kWB, wb = wave % kWB;
-
-    // ---- tile order: XCD-aware, grouped 4 W tiles x all X tiles
-    const int nwg = gridDim.x;
-    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    const int per_xcd = (nwg + 7) >> 3, full = nwg & 7 ? (nwg & 7) : 8;
-    const int t = xcd < full ? xcd * per_xcd + local : full * per_xcd + (xcd - full) * (per_xcd - 1) + local;
-    constexpr int G = 8;
-    const int group = t / (G * tiles_b), within = t - group * G * tiles_b;
-    const int g_rows = min(G, tiles_a - group * G);
-    const int ta = group * G + within % g_rows, tb = within / g_rows;
-    const int a0 = ta * kBA, b0 = tb * kBB;
 
     const uint32_t row_bytes = (uint32_t)K * (DT == SP24_E4M3 || DT == SP24_I8 ? 1 : 2);
     const int steps = (int)((row_bytes + 127) / 128);   // the last may be partial
@@ -233,6 +241,42 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
 }
 
 template <sp24_dtype DT, sp24_dtype OUT, class TL>
+__global__ void __launch_bounds__(TL::THREADS, TL::OCC)
+dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
+          const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K, int tiles_a,
+          int tiles_b) {
+    __shared__ __attribute__((aligned(1024))) uint8_t a0s[TL::BA * 128], a1s[TL::BA * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t b0s[TL::BB * 128], b1s[TL::BB * 128];
+    const DTilePos p = dtile_pos(dxcd_order((int)blockIdx.x, (int)gridDim.x), tiles_a, tiles_b);
+    dense_tile<DT, OUT, TL>(a0s, a1s, b0s, b1s, W, X, sx, sw, Y, N, M, K, p.ta * TL::BA, p.tb * TL::BB, p.group);
+}
+
+// The 256 x 256 grid with a short last round, as the sparse tile kernels run
+// it: the first n_big tiles (whole rounds) as 256 x 256, each later tile as
+// four 128 x 128 quarters, in the big tile's LDS.
+template <sp24_dtype DT, sp24_dtype OUT>
+__global__ void __launch_bounds__(D256x256::THREADS, 1)
+dense_big_tail(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
+               const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K, int tiles_a,
+               int tiles_b, int n_big) {
+    static_assert(D128x128::THREADS == D256x256::THREADS, "one block size");
+    __shared__ __attribute__((aligned(1024))) uint8_t a0s[256 * 128], a1s[256 * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t b0s[256 * 128], b1s[256 * 128];
+    const int b = (int)blockIdx.x;
+    if (b < n_big) {
+        const DTilePos p = dtile_pos(dxcd_order(b, n_big), tiles_a, tiles_b);
+        dense_tile<DT, OUT, D256x256>(a0s, a1s, b0s, b1s, W, X, sx, sw, Y, N, M, K, p.ta * 256, p.tb * 256,
+                                      p.group);
+    } else {
+        // n_big is a multiple of 8, so b - n_big keeps b's XCD
+        const int q = dxcd_order(b - n_big, (int)gridDim.x - n_big);
+        const DTilePos p = dtile_pos(n_big + q / 4, tiles_a, tiles_b);
+        dense_tile<DT, OUT, D128x128>(a0s, a1s, b0s, b1s, W, X, sx, sw, Y, N, M, K,
+                                      p.ta * 256 + 128 * ((q >> 1) & 1), p.tb * 256 + 128 * (q & 1), p.group);
+    }
+}
+
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
 hipError_t launch_tile(const DenseArgs& g, hipStream_t s, const char** kname, const char* name) {
     const int N = (int)g.N, M = (int)g.M;
     const int tiles_a = (N + TL::BA - 1) / TL::BA, tiles_b = (M + TL::BB - 1) / TL::BB;
@@ -246,18 +290,36 @@ hipError_t launch_tile(const DenseArgs& g, hipStream_t s, const char** kname, co
     return hipGetLastError();
 }
 
+template <sp24_dtype DT, sp24_dtype OUT>
+hipError_t launch_tail(const DenseArgs& g, hipStream_t s, const char** kname, int64_t n_big, int64_t n_split) {
+    const int N = (int)g.N, M = (int)g.M;
+    const int tiles_a = (N + 255) / 256, tiles_b = (M + 255) / 256;
+    if (kname)
+        *kname = "dense_big_256x256_tail";
+    if (g.dry)
+        return hipSuccess;
+    hipLaunchKernelGGL((dense_big_tail<DT, OUT>), dim3((unsigned)(n_big + 4 * n_split)), dim3(D256x256::THREADS), 0,
+                       s, (const uint8_t*)g.W, (const uint8_t*)g.X, g.scale_x, g.scale_w, g.Y, N, M, g.K, tiles_a,
+                       tiles_b, (int)n_big);
+    return hipGetLastError();
+}
+
 template <class TL>
 int64_t tiles_of(const DenseArgs& g) {
     return ((g.N + TL::BA - 1) / TL::BA) * ((g.M + TL::BB - 1) / TL::BB) * TL::OCC;
 }
 
 // The same tile choice as the sparse kernels: the largest tile that keeps
-// most CUs busy (192 workgroups), else the smallest.
+// most CUs busy (192 workgroups), else the smallest; a short last round of
+// 256 x 256 tiles (at most a quarter of the chip) as quarter tiles.
 template <sp24_dtype DT, sp24_dtype OUT>
 hipError_t launch(const DenseArgs& g, hipStream_t s, const char** kname) {
     constexpr int64_t kFill = 192;
+    constexpr int64_t kCUs = 256;   // compute units of the gfx950 parts (MI350X, MI355X)
     if (g.M > 64) {
-        if (tiles_of<D256x256>(g) >= kFill) return launch_tile<DT, OUT, D256x256>(g, s, kname, "dense_big_256x256");
+        const int64_t t256 = tiles_of<D256x256>(g), rest = t256 % kCUs;
+        if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs) return launch_tail<DT, OUT>(g, s, kname, t256 - rest, rest);
+        if (t256 >= kFill) return launch_tile<DT, OUT, D256x256>(g, s, kname, "dense_big_256x256");
         if (tiles_of<D256x128>(g) >= kFill) return launch_tile<DT, OUT, D256x128>(g, s, kname, "dense_big_256x128");
         return launch_tile<DT, OUT, D128x128>(g, s, kname, "dense_big_128x128");
     }

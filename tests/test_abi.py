@@ -125,6 +125,14 @@ def test_gemm_kernel_names_follow_the_dispatch():
     assert k(False, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "dense_skinny_m1"
     # beyond 16 rows: the largest LDS-staged tile that still fills the chip
     assert k(True, sp.SPARSE_W, bf, bf, 8192, 4096, 4096) == "sp24_big_256x256"
+    # more than one round of 256x256 tiles, the last at most a quarter of the chip: quarter tiles
+    assert k(True, sp.SPARSE_W, bf, bf, 4096, 5120, 5120) == "sp24_big_256x256_tail"        # 320 = 256 + 64
+    assert k(True, sp.SPARSE_W, bf, bf, 4096, 4352, 4096) == "sp24_big_256x256_tail"        # 272 = 256 + 16
+    assert k(True, sp.SPARSE_X, bf, bf, 5120, 4096, 4096) == "sp24_big_256x256_tail"        # A = X: 20 x 16
+    assert k(True, sp.SPARSE_W, bf, bf, 2048, 28672, 4096) == "sp24_big_256x256"            # 896 = 3 * 256 + 128
+    assert k(True, sp.SPARSE_W, bf, bf, 2048, 6144, 4096) == "sp24_big_256x256"             # 192: one round
+    assert k(False, sp.SPARSE_W, bf, bf, 4096, 5120, 5120) == "dense_big_256x256_tail"
+    assert k(False, sp.SPARSE_W, bf, bf, 2048, 28672, 4096) == "dense_big_256x256"
     assert k(True, sp.SPARSE_W, bf, bf, 2048, 4096, 4096) == "sp24_big_256x128"
     assert k(True, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "sp24_big_128x128"
     assert k(True, sp.SPARSE_W, bf, bf, 64, 28672, 4096) == "sp24_big_128x64"

@@ -222,6 +222,52 @@ def test_large_tile_kernels_ragged(dt, which, steps, MN):
     assert np.array_equal(decode_out(Y[torch.from_numpy(rows).cuda()]), R)
 
 
+# 256x256 grids with a short last round, whose remainder runs as quarter
+# tiles: (M, N, K steps) with ragged last tiles in both dimensions
+TAIL = [(4066, 4302, 6), (4096, 5120 - 40, 7), (1000, 68 * 256 - 7, 5)]
+
+
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.E4M3])
+@pytest.mark.parametrize("which", ["sparse_w", "sparse_x", "dense"])
+@pytest.mark.parametrize("M,N,steps", TAIL)
+def test_tail_quarter_tiles(dt, which, M, N, steps):
+    """The 256x256 kernels (sparse and dense) with their last round split
+    into 128x128 quarter tiles: integer inputs, rows sampled from every
+    256-row band of the output (both halves of each), bitwise equal to the
+    oracle, and every output written."""
+    K = steps * (64 if dt != oracle.E4M3 else 128)
+    RA, RB = (M, N) if which == "sparse_x" else (N, M)
+    t = ((RA + 255) // 256) * ((RB + 255) // 256)
+    assert t > 256 and 0 < t % 256 <= 64, t
+    ttype = {oracle.BF16: torch.bfloat16, oracle.E4M3: torch.float8_e4m3fn}[dt]
+    op = sp.SPARSE_X if which == "sparse_x" else sp.SPARSE_W
+    name = "dense_big_256x256_tail" if which == "dense" else "sp24_big_256x256_tail"
+    assert sp.gemm_kernel(which != "dense", op, ttype, torch.float32, M, N, K) == name
+    say("tail quarters", which, dt, M, N, K)
+    xb, _, wb, _ = _operands(dt, M, N, K, 321, integer=True)
+    rows = np.unique(np.clip(np.concatenate([np.arange(0, M, 256), np.arange(129, M, 256),
+                                             np.arange(255, M, 256), [M - 1]]), 0, M - 1))
+    X, W = to_dev(xb, dt), to_dev(wb, dt)
+    Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    if which == "sparse_w":
+        wv, wm = oracle.prune_compress(dt, wb)
+        R = oracle.gemm(dt, M, N, K, x=xb, w_vals=wv, w_meta=wm, mrows=rows)
+        v, m = sp.prune_compress(W)
+        sp.sp24_gemm(sp.SPARSE_W, v, m, X, M, N, K, out=Y)
+    elif which == "sparse_x":
+        xv, xm = oracle.prune_compress(dt, xb)
+        R = oracle.gemm(dt, M, N, K, x_vals=xv, x_meta=xm, w=wb, mrows=rows)
+        v, m = sp.prune_compress(X)
+        sp.sp24_gemm(sp.SPARSE_X, v, m, W, M, N, K, out=Y)
+    else:
+        R = oracle.gemm(dt, M, N, K, x=xb, w=wb, mrows=rows)
+        sp.dense_gemm(X, W, out=Y)
+    torch.cuda.synchronize()
+    assert np.array_equal(decode_out(Y[torch.from_numpy(rows).cuda()]), R)
+    # every tile wrote its outputs: none is left at the NaN it started with
+    assert torch.isfinite(Y).all()
+
+
 def test_one_hot_rows_read_back_weights():
     """X = identity rows: Y[m, :] is column m of the decompressed W, which
     checks every metadata position and word through the sparse MMA."""
