@@ -319,8 +319,12 @@ hipError_t launch(const DenseArgs& g, hipStream_t s, const char** kname) {
     if (g.M > 64) {
         const int64_t t256 = tiles_of<D256x256>(g), rest = t256 % kCUs;
         if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs) return launch_tail<DT, OUT>(g, s, kname, t256 - rest, rest);
-        if (t256 >= kFill) return launch_tile<DT, OUT, D256x256>(g, s, kname, "dense_big_256x256");
-        if (tiles_of<D256x128>(g) >= kFill) return launch_tile<DT, OUT, D256x128>(g, s, kname, "dense_big_256x128");
+        // between 256 x 256 and 256 x 128: the cheaper rounds, as the sparse kernels choose
+        const int64_t t128 = tiles_of<D256x128>(g);
+        const int64_t r256 = (t256 + kCUs - 1) / kCUs, r128 = (t128 + kCUs - 1) / kCUs;
+        if (t256 >= kFill || (t128 >= kFill && 10 * r256 <= 7 * r128))
+            return launch_tile<DT, OUT, D256x256>(g, s, kname, "dense_big_256x256");
+        if (t128 >= kFill) return launch_tile<DT, OUT, D256x128>(g, s, kname, "dense_big_256x128");
         return launch_tile<DT, OUT, D128x128>(g, s, kname, "dense_big_128x128");
     }
     if (tiles_of<D256x64>(g) >= kFill) return launch_tile<DT, OUT, D256x64>(g, s, kname, "dense_big_256x64");

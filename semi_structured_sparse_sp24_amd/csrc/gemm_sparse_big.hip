@@ -468,6 +468,16 @@ hipError_t launch_tail(const GemmArgs& g, hipStream_t s, const char** kname, int
     return hipGetLastError();
 }
 
+// Between 256 x 256 and 256 x 128 tiles when the big ones alone would not
+// fill the chip: the one whose rounds cost less, a round of 256 x 128 tiles
+// counted as 0.7 of a round of 256 x 256 ones (measured 0.66-0.75 on the
+// bf16 prefill shapes).  So a 256 x 256 grid of one round beats a 256 x 128
+// grid of two.
+inline bool prefer_256(int64_t t256, int64_t t128, int64_t cus) {
+    const int64_t r256 = (t256 + cus - 1) / cus, r128 = (t128 + cus - 1) / cus;
+    return 10 * r256 <= 7 * r128;
+}
+
 template <class TL>
 int64_t tiles_of(const GemmArgs& g) {
     const int64_t RA = g.a_is_w ? g.N : g.M, RB = g.a_is_w ? g.M : g.N;
@@ -490,8 +500,10 @@ hipError_t launch_big(const GemmArgs& g, hipStream_t s, const char** kname) {
         // to quarter tiles (measured: 20-32% faster at remainders of 16 and 64
         // tiles; at 128, two rounds of quarters, -1% bf16 to +2.5% fp8)
         if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs) return launch_tail<DT, OUT>(g, s, kname, t256 - rest, rest);
-        if (t256 >= kFill) return launch_tile<DT, OUT, T256x256>(g, s, kname, "sp24_big_256x256");
-        if (tiles_of<T256x128>(g) >= kFill) return launch_tile<DT, OUT, T256x128>(g, s, kname, "sp24_big_256x128");
+        const int64_t t128 = tiles_of<T256x128>(g);
+        if (t256 >= kFill || (t128 >= kFill && prefer_256(t256, t128, kCUs)))
+            return launch_tile<DT, OUT, T256x256>(g, s, kname, "sp24_big_256x256");
+        if (t128 >= kFill) return launch_tile<DT, OUT, T256x128>(g, s, kname, "sp24_big_256x128");
         return launch_tile<DT, OUT, T128x128>(g, s, kname, "sp24_big_128x128");
     }
     if (tiles_of<T256x64>(g) >= kFill) return launch_tile<DT, OUT, T256x64>(g, s, kname, "sp24_big_256x64");
@@ -525,10 +537,12 @@ int64_t hybrid_tiles_of(const HybridArgs& h) {
 template <sp24_dtype DT, sp24_dtype OUT>
 hipError_t launch_hybrid(const HybridArgs& h, hipStream_t s, const char** kname) {
     constexpr int64_t kFill = 192;
+    constexpr int64_t kCUs = 256;
     if (h.M > 64) {
-        if (hybrid_tiles_of<T256x256>(h) >= kFill)
+        const int64_t t256 = hybrid_tiles_of<T256x256>(h), t128 = hybrid_tiles_of<T256x128>(h);
+        if (t256 >= kFill || (t128 >= kFill && prefer_256(t256, t128, kCUs)))
             return launch_hybrid_tile<DT, OUT, T256x256>(h, s, kname, "sp24_hybrid_256x256");
-        if (hybrid_tiles_of<T256x128>(h) >= kFill)
+        if (t128 >= kFill)
             return launch_hybrid_tile<DT, OUT, T256x128>(h, s, kname, "sp24_hybrid_256x128");
         return launch_hybrid_tile<DT, OUT, T128x128>(h, s, kname, "sp24_hybrid_128x128");
     }

@@ -133,6 +133,10 @@ def test_gemm_kernel_names_follow_the_dispatch():
     assert k(True, sp.SPARSE_W, bf, bf, 2048, 6144, 4096) == "sp24_big_256x256"             # 192: one round
     assert k(False, sp.SPARSE_W, bf, bf, 4096, 5120, 5120) == "dense_big_256x256_tail"
     assert k(False, sp.SPARSE_W, bf, bf, 2048, 28672, 4096) == "dense_big_256x256"
+    # 160 tiles of 256x256 (one round) against 320 of 256x128 (two): the big ones
+    assert k(True, sp.SPARSE_W, bf, bf, 2048, 5120, 4096) == "sp24_big_256x256"
+    assert k(False, sp.SPARSE_W, bf, bf, 2048, 5120, 4096) == "dense_big_256x256"
+    assert k(True, sp.SPARSE_W, bf, bf, 2048, 4096, 4096) == "sp24_big_256x128"
     assert k(True, sp.SPARSE_W, bf, bf, 2048, 4096, 4096) == "sp24_big_256x128"
     assert k(True, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "sp24_big_128x128"
     assert k(True, sp.SPARSE_W, bf, bf, 64, 28672, 4096) == "sp24_big_128x64"
@@ -267,6 +271,9 @@ def test_hybrid_validation_precedes_hip():
     k = sp.hybrid_kernel
     bf = __import__("torch").bfloat16
     assert k(bf, bf, 4096, 4096, 1024, 4096) == "sp24_hybrid_256x256"
+    # 144 tiles of 256x256 (one round) against 288 of 256x128 (two): the big ones
+    assert k(bf, bf, 2048, 3584, 512, 4096) == "sp24_hybrid_256x256"
+    assert k(bf, bf, 1536, 2048, 1024, 4096) == "sp24_hybrid_256x128"
     assert k(bf, bf, 64, 4096, 512, 4096) == "sp24_hybrid_128x64"
     assert k(bf, bf, 64, 49152, 512, 4096) == "sp24_hybrid_256x64"
     assert k(bf, bf, 512, 512, 256, 4096) == "sp24_hybrid_128x128"
