@@ -29,6 +29,22 @@ hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Enum arguments come from C callers as ints, and C allows any int value
+// there; C++ does not allow reading a value outside the enumeration's range
+// as that enumeration.  Every entry point therefore reads an enum argument's
+// bytes as an int and checks it before it uses the argument as the enum (the
+// helpers it forwards to take the arguments by reference, so forwarding
+// reads nothing).
+template <class E>
+int enum_bits(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "the enums are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+bool dtype_known(int v) { return v >= SP24_F16 && v <= SP24_I8; }
+bool operand_known(int v) { return v == SP24_SPARSE_W || v == SP24_SPARSE_X; }
+
 bool is_input_dtype(int dt) { return dt == SP24_F16 || dt == SP24_BF16 || dt == SP24_E4M3 || dt == SP24_I8; }
 
 bool out_ok(sp24_dtype in, sp24_dtype out) {
@@ -121,7 +137,7 @@ SP24_API int64_t sp24_meta_words_per_row(int64_t K) { return K < 0 ? 0 : meta_wo
 SP24_API sp24_status sp24_prune_compress(sp24_dtype dt, int64_t rows, int64_t K, const void* src,
                                          int64_t ld_src, void* values, uint32_t* meta,
                                          hipStream_t stream) {
-    if (!is_input_dtype(dt))
+    if (!dtype_known(enum_bits(dt)) || !is_input_dtype(dt))
         return SP24_E_DTYPE;
     if (rows < 0 || K < 0 || K % 4 != 0 || ld_src < K)
         return SP24_E_SHAPE;
@@ -136,7 +152,7 @@ SP24_API sp24_status sp24_prune_compress(sp24_dtype dt, int64_t rows, int64_t K,
 SP24_API sp24_status sp24_decompress(sp24_dtype dt, int64_t rows, int64_t K, const void* values,
                                      const uint32_t* meta, void* dst, int64_t ld_dst,
                                      hipStream_t stream) {
-    if (!is_input_dtype(dt))
+    if (!dtype_known(enum_bits(dt)) || !is_input_dtype(dt))
         return SP24_E_DTYPE;
     if (rows < 0 || K < 0 || K % 4 != 0 || ld_dst < K)
         return SP24_E_SHAPE;
@@ -151,9 +167,9 @@ SP24_API sp24_status sp24_decompress(sp24_dtype dt, int64_t rows, int64_t K, con
 // one 256-lane workgroup per row: the grid stays below 2^32 lanes
 static constexpr int64_t kMaxQuantRows = (int64_t)1 << 24;
 
-static sp24_status quantize_impl(sp24_dtype dt, int64_t rows, int64_t K, const void* src, int64_t ld_src,
+static sp24_status quantize_impl(const sp24_dtype& dt, int64_t rows, int64_t K, const void* src, int64_t ld_src,
                                  void* out, uint32_t* meta, float* scales, bool prune, hipStream_t stream) {
-    if (dt != SP24_F16 && dt != SP24_BF16)
+    if (!dtype_known(enum_bits(dt)) || (dt != SP24_F16 && dt != SP24_BF16))
         return SP24_E_DTYPE;
     if (rows < 0 || K < 0 || ld_src < K || rows > kMaxQuantRows)
         return SP24_E_SHAPE;
@@ -179,12 +195,14 @@ SP24_API sp24_status sp24_quantize_e4m3(sp24_dtype src_dt, int64_t rows, int64_t
     return quantize_impl(src_dt, rows, K, src, ld_src, dst, nullptr, scales, false, stream);
 }
 
-static sp24_status gemm_impl(sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt, int64_t M,
+static sp24_status gemm_impl(const sp24_operand& which, const sp24_dtype& in_dt, const sp24_dtype& out_dt, int64_t M,
                              int64_t N, int64_t K, const void* values, const uint32_t* meta,
                              const void* dense, const float* scale_x, const float* scale_w, void* Y,
                              hipStream_t stream, const char** kname) {
-    if (which != SP24_SPARSE_W && which != SP24_SPARSE_X)
+    if (!operand_known(enum_bits(which)))
         return SP24_E_SHAPE;
+    if (!dtype_known(enum_bits(in_dt)) || !dtype_known(enum_bits(out_dt)))
+        return SP24_E_DTYPE;
     sp24_status st = check_gemm(in_dt, out_dt, M, N, K, {values, meta, dense}, Y, scale_x, scale_w, true);
     if (st != SP24_OK)
         return st;
@@ -210,9 +228,11 @@ static sp24_status gemm_impl(sp24_operand which, sp24_dtype in_dt, sp24_dtype ou
     return launch_sp24_gemm(g, stream, kname) == hipSuccess ? SP24_OK : SP24_E_HIP;
 }
 
-static sp24_status dense_impl(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K,
+static sp24_status dense_impl(const sp24_dtype& in_dt, const sp24_dtype& out_dt, int64_t M, int64_t N, int64_t K,
                               const void* X, const void* W, const float* scale_x, const float* scale_w,
                               void* Y, hipStream_t stream, const char** kname) {
+    if (!dtype_known(enum_bits(in_dt)) || !dtype_known(enum_bits(out_dt)))
+        return SP24_E_DTYPE;
     sp24_status st = check_gemm(in_dt, out_dt, M, N, K, {X, W}, Y, scale_x, scale_w, false);
     if (st != SP24_OK)
         return st;
@@ -237,9 +257,10 @@ static sp24_status dense_impl(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, in
 }
 
 // Dtype and size checks of the hybrid GEMM (no pointer is looked at).
-static sp24_status check_hybrid_shape(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t NS, int64_t ND,
+static sp24_status check_hybrid_shape(const sp24_dtype& in_dt, const sp24_dtype& out_dt, int64_t M, int64_t NS, int64_t ND,
                                       int64_t K) {
-    if (!is_input_dtype(in_dt) || !out_ok(in_dt, out_dt))
+    if (!dtype_known(enum_bits(in_dt)) || !dtype_known(enum_bits(out_dt)) || !is_input_dtype(in_dt) ||
+        !out_ok(in_dt, out_dt))
         return SP24_E_DTYPE;
     if (NS < 0 || ND < 0 || NS > INT32_MAX / 2 - ND)
         return SP24_E_SHAPE;
@@ -256,7 +277,8 @@ SP24_API sp24_status sp24_hybrid_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64
                                       int64_t K, const void* values, const uint32_t* meta, const void* W_d,
                                       const void* X, const float* scale_x, const float* scale_w, void* Y,
                                       hipStream_t stream) {
-    if (!is_input_dtype(in_dt) || !out_ok(in_dt, out_dt))
+    if (!dtype_known(enum_bits(in_dt)) || !dtype_known(enum_bits(out_dt)) || !is_input_dtype(in_dt) ||
+        !out_ok(in_dt, out_dt))
         return SP24_E_DTYPE;
     if (M < 0 || N_s < 0 || N_d < 0 || K < 0 || K % 4 != 0)
         return SP24_E_SHAPE;
@@ -315,7 +337,10 @@ SP24_API const char* sp24_hybrid_kernel(sp24_dtype in_dt, sp24_dtype out_dt, int
 
 SP24_API const char* sp24_gemm_kernel(int sparse, sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt,
                                      int64_t M, int64_t N, int64_t K) {
-    if (sparse && which != SP24_SPARSE_W && which != SP24_SPARSE_X)
+    const int w = enum_bits(which);
+    if (sparse && !operand_known(w))
+        return nullptr;
+    if (!dtype_known(enum_bits(in_dt)) || !dtype_known(enum_bits(out_dt)))
         return nullptr;
     if (check_shape(in_dt, out_dt, M, N, K, sparse != 0) != SP24_OK)
         return nullptr;
@@ -331,7 +356,7 @@ SP24_API const char* sp24_gemm_kernel(int sparse, sp24_operand which, sp24_dtype
         g.M = M;
         g.N = N;
         g.K = K;
-        g.a_is_w = which == SP24_SPARSE_W;
+        g.a_is_w = w == SP24_SPARSE_W;
         g.dry = true;
         launch_sp24_gemm(g, nullptr, &name);
     } else {
@@ -438,8 +463,10 @@ SP24_API sp24_status sp24_select_tactic(sp24_operand which, sp24_dtype in_dt, sp
     memset(out, 0, sizeof(*out));
     if (reps < 1 || warmup < 0)
         return SP24_E_SHAPE;
-    if (which != SP24_SPARSE_W && which != SP24_SPARSE_X)
+    if (!operand_known(enum_bits(which)))
         return SP24_E_SHAPE;
+    if (!dtype_known(enum_bits(in_dt)) || !dtype_known(enum_bits(out_dt)))
+        return SP24_E_DTYPE;
     // eligibility of the sparse path
     int eligible = 1;
     if (!is_input_dtype(in_dt) || !out_ok(in_dt, out_dt)) {
