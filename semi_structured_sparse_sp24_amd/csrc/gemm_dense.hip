@@ -73,38 +73,46 @@ struct DenseOp16<SP24_E4M3> {
 // ------------------------------------------------------------------ skinny
 constexpr int kMaxWaves = 16;
 
-template <sp24_dtype DT, sp24_dtype OUT, int MT, int U>
+// MT: 16-row blocks of X per pass; U: K steps per load batch; AT: 16-row
+// tiles of W per workgroup (2 halves the X traffic per W byte, as in the
+// sparse decode kernel).
+template <sp24_dtype DT, sp24_dtype OUT, int MT, int U, int AT>
 __global__ void __launch_bounds__(kMaxWaves * 64)
 dense_skinny(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
              const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K) {
     using Op = DenseOp16<DT>;
     constexpr int STEP_BYTES = Op::KSTEP * Op::ELEM;   // 128
-    __shared__ float red[kMaxWaves][MT][4][64];
+    __shared__ float red[kMaxWaves][AT][MT][4][64];
     const int WAVES = blockDim.x >> 6;   // 4, 8 or 16: the waves split K
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, kg = lane >> 4;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * 16 * AT;
     const int steps = (int)((K + Op::KSTEP - 1) / Op::KSTEP);   // the last step may be partial
     const int64_t row_bytes = K * Op::ELEM;
     const int o0 = 16 * kg, o1 = STEP_BYTES / 2 + 16 * kg;
 
     const Buf bufW(W, (uint32_t)N * (uint32_t)row_bytes);   // rows past N / M read as zeros
     const Buf bufX(X, (uint32_t)M * (uint32_t)row_bytes);
-    const uint32_t a_base = (uint32_t)(n0 + r) * (uint32_t)row_bytes;
+    uint32_t a_base[AT];
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+        a_base[t] = (uint32_t)(n0 + 16 * t + r) * (uint32_t)row_bytes;
     uint32_t b_base[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
         b_base[mt] = (uint32_t)(mt * 16 + r) * (uint32_t)row_bytes;
-    f32x4 acc[MT];
+    f32x4 acc[AT][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < AT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[t][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     // contiguous K chunk per wave, K loop rotated per workgroup (as in the
     // sparse kernel)
     const int chunk = (steps + WAVES - 1) / WAVES;
     const int rot = (int)((blockIdx.x * 13u) % (unsigned)max(steps, 1));
     for (int i0 = 0; i0 < chunk; i0 += U) {
-        uint4 a0[U], a1[U], b0[U][MT], b1[U][MT];
+        uint4 a0[U][AT], a1[U][AT], b0[U][MT], b1[U][MT];
         bool live[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -117,8 +125,11 @@ dense_skinny(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const
             const bool in0 = live[u] && k0 + o0 < row_bytes;
             const bool in1 = live[u] && k0 + o1 < row_bytes;
             const uint32_t d0 = in0 ? (uint32_t)(k0 + o0) : kOOB, d1 = in1 ? (uint32_t)(k0 + o1) : kOOB;
-            a0[u] = bufW.ld16(a_base + d0);
-            a1[u] = bufW.ld16(a_base + d1);
+#pragma unroll
+            for (int t = 0; t < AT; ++t) {
+                a0[u][t] = bufW.ld16(a_base[t] + d0);
+                a1[u][t] = bufW.ld16(a_base[t] + d1);
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 b0[u][mt] = bufX.ld16(b_base[mt] + d0);
@@ -130,29 +141,35 @@ dense_skinny(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const
             if (live[u])
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    acc[mt] = Op::mma(a0[u], a1[u], b0[u][mt], b1[u][mt], acc[mt]);
+#pragma unroll
+                    for (int t = 0; t < AT; ++t)
+                        acc[t][mt] = Op::mma(a0[u][t], a1[u][t], b0[u][mt], b1[u][mt], acc[t][mt]);
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < AT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            red[wave][mt][i][lane] = acc[mt][i];
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                red[wave][t][mt][i][lane] = acc[t][mt][i];
     __syncthreads();
-    for (int o = threadIdx.x; o < 16 * 16 * MT; o += WAVES * 64) {
-        const int al = o & 15, bl = o >> 4;
+    constexpr int TILE = 16 * 16 * MT;
+    for (int o = threadIdx.x; o < AT * TILE; o += WAVES * 64) {
+        const int t = o / TILE, ot = o - t * TILE;
+        const int al = ot & 15, bl = ot >> 4;
         const int mt = bl >> 4, ln = ((al >> 2) << 4) | (bl & 15), i = al & 3;
         float v = 0.f;
         if constexpr (DT == SP24_I8) {
             // int32 partial sums (their bits in red): added exactly, converted once
             int vi = 0;
             for (int w = 0; w < WAVES; ++w)
-                vi += __builtin_bit_cast(int, red[w][mt][i][ln]);
+                vi += __builtin_bit_cast(int, red[w][t][mt][i][ln]);
             v = (float)vi;
         } else {
             for (int w = 0; w < WAVES; ++w)   // fixed order: deterministic
-                v += red[w][mt][i][ln];
+                v += red[w][t][mt][i][ln];
         }
-        const int n = n0 + al, m = bl;
+        const int n = n0 + 16 * t + al, m = bl;
         if (n < N && m < M) {
             if (sx)
                 v *= sx[m];
@@ -173,20 +190,27 @@ hipError_t dispatch(const DenseArgs& g, hipStream_t s, const char** kname) {
     if (M <= 16 || (M <= 64 && (N + 127) / 128 < 128)) {
         const int tiles16 = (N + 15) / 16;
         const int steps = (int)((g.K + DenseOp16<DT>::KSTEP - 1) / DenseOp16<DT>::KSTEP);
+        const int mt = (M + 15) / 16;
+        const bool a32 = mt >= 2 && tiles16 / 2 >= 160;
+        const int64_t wgs = a32 ? (tiles16 + 1) / 2 : tiles16;
         int waves = 16;
-        while (waves > 4 && ((int64_t)tiles16 * waves > 8192 || steps < waves * 2))
+        while (waves > 4 && (wgs * waves > 8192 || steps < waves * 2))
             waves >>= 1;
-#define DENSE_SKINNY(MT, U)                                                                          \
+#define DENSE_SKINNY(MT, U, AT, NAME)                                                                \
     do {                                                                                             \
         if (!g.dry)                                                                                  \
-            hipLaunchKernelGGL((dense_skinny<DT, OUT, MT, U>), dim3(tiles16), dim3(waves * 64), 0, s,  \
-                               W, X, g.scale_x, g.scale_w, g.Y, N, M, g.K);                          \
-        if (kname) *kname = "dense_skinny_m" #MT;                                                    \
+            hipLaunchKernelGGL((dense_skinny<DT, OUT, MT, U, AT>), dim3((N + 16 * AT - 1) / (16 * AT)),  \
+                               dim3(waves * 64), 0, s, W, X, g.scale_x, g.scale_w, g.Y, N, M, g.K);  \
+        if (kname) *kname = NAME;                                                                    \
     } while (0)
-        const int mt = (M + 15) / 16;
-        if (mt <= 1) DENSE_SKINNY(1, 4);
-        else if (mt == 2) DENSE_SKINNY(2, 2);
-        else DENSE_SKINNY(4, 2);
+        // 17 to 64 rows of X: 32-row W tiles when that still leaves 160 or more
+        // workgroups (each X fragment then serves two W tiles), as the sparse
+        // decode kernel does
+        if (mt <= 1) DENSE_SKINNY(1, 4, 1, "dense_skinny_m1");
+        else if (mt == 2 && a32) DENSE_SKINNY(2, 2, 2, "dense_skinny_m2_a32");
+        else if (mt == 2) DENSE_SKINNY(2, 2, 1, "dense_skinny_m2");
+        else if (a32) DENSE_SKINNY(4, 2, 2, "dense_skinny_m4_a32");
+        else DENSE_SKINNY(4, 2, 1, "dense_skinny_m4");
 #undef DENSE_SKINNY
     } else {
         return launch_dense_gemm_big(g, s, kname);

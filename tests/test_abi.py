@@ -122,6 +122,12 @@ def test_gemm_kernel_names_follow_the_dispatch():
     assert k(True, sp.SPARSE_W, bf, bf, 4, 4096, 4096) == "sp24_skinny_x4"
     assert k(True, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "sp24_skinny_m16"
     assert k(True, sp.SPARSE_W, bf, bf, 64, 4096, 4096) == "sp24_skinny_m64"
+    # 17 to 64 rows: 32-row A tiles once there are 160 of them (5120 rows of W and more)
+    assert k(True, sp.SPARSE_W, bf, bf, 64, 6144, 4096) == "sp24_skinny_m64_a32"
+    assert k(True, sp.SPARSE_W, bf, bf, 32, 5120, 4096) == "sp24_skinny_m32_a32"
+    assert k(True, sp.SPARSE_W, bf, bf, 32, 5104, 4096) == "sp24_skinny_m32"
+    assert k(False, sp.SPARSE_W, bf, bf, 64, 6144, 4096) == "dense_skinny_m4_a32"
+    assert k(False, sp.SPARSE_W, bf, bf, 32, 5120, 4096) == "dense_skinny_m2_a32"
     assert k(False, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "dense_skinny_m1"
     # beyond 16 rows: the largest LDS-staged tile that still fills the chip
     assert k(True, sp.SPARSE_W, bf, bf, 8192, 4096, 4096) == "sp24_big_256x256"

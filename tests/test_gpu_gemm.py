@@ -141,7 +141,10 @@ SKINNY = [(1, 100, 704, "sp24_skinny_x4"), (4, 6150, 704, "sp24_skinny_x4"),
           (9, 300, 704, "sp24_skinny_m16"), (16, 6150, 704, "sp24_skinny_m16_a32"),
           (7, 6166, 1216, "sp24_skinny_m16_a32"), (30, 200, 704, "sp24_skinny_m32"),
           (64, 190, 704, "sp24_skinny_m64"), (50, 333, 192, "sp24_skinny_m64"),
-          (40, 17000, 704, "sp24_big_128x64"), (17, 61500, 192, "sp24_big_256x64")]
+          (40, 17000, 704, "sp24_big_128x64"), (17, 61500, 192, "sp24_big_256x64"),
+          # 32-row A tiles for 17 to 64 rows once there are 160 or more of them
+          (30, 6150, 704, "sp24_skinny_m32_a32"), (64, 5200, 704, "sp24_skinny_m64_a32"),
+          (50, 5130, 192, "sp24_skinny_m64_a32")]
 
 
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
@@ -158,7 +161,8 @@ def test_skinny_variants_exact(dt, M, N, K, kernel):
 
 
 DENSE_FEW = [(40, 17000, 704, "dense_big_128x64"), (17, 61500, 200, "dense_big_256x64"),
-             (64, 190, 704, "dense_skinny_m4"), (20, 300, 200, "dense_skinny_m2")]
+             (64, 190, 704, "dense_skinny_m4"), (20, 300, 200, "dense_skinny_m2"),
+             (64, 5200, 704, "dense_skinny_m4_a32"), (20, 6150, 200, "dense_skinny_m2_a32")]
 
 
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
