@@ -61,9 +61,6 @@ using T128x64 = Tile<128, 64, 4, 2, 2>;
 __device__ __forceinline__ void dma16(const Buf& b, void* lds_base, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_void*)lds_base, 16, (int)voff, (int)soff, 0, 0);
 }
-__device__ __forceinline__ void dma4(const Buf& b, void* lds_base, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_void*)lds_base, 4, (int)voff, (int)soff, 0, 0);
-}
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits [3:0] and
 // [15:14], expcnt [6:4], lgkmcnt [11:8]).
