@@ -325,7 +325,9 @@ hipError_t launch(const DenseArgs& g, hipStream_t s, const char** kname) {
         if (t256 >= kFill || (t128 >= kFill && 10 * r256 <= 7 * r128))
             return launch_tile<DT, OUT, D256x256>(g, s, kname, "dense_big_256x256");
         if (t128 >= kFill) return launch_tile<DT, OUT, D256x128>(g, s, kname, "dense_big_256x128");
-        return launch_tile<DT, OUT, D128x128>(g, s, kname, "dense_big_128x128");
+        if (tiles_of<D128x128>(g) / D128x128::OCC >= kFill)
+            return launch_tile<DT, OUT, D128x128>(g, s, kname, "dense_big_128x128");
+        return launch_tile<DT, OUT, D128x64>(g, s, kname, "dense_big_128x64");
     }
     if (tiles_of<D256x64>(g) >= kFill) return launch_tile<DT, OUT, D256x64>(g, s, kname, "dense_big_256x64");
     return launch_tile<DT, OUT, D128x64>(g, s, kname, "dense_big_128x64");

@@ -501,7 +501,11 @@ hipError_t launch_big(const GemmArgs& g, hipStream_t s, const char** kname) {
         if (t256 >= kFill || (t128 >= kFill && prefer_256(t256, t128, kCUs)))
             return launch_tile<DT, OUT, T256x256>(g, s, kname, "sp24_big_256x256");
         if (t128 >= kFill) return launch_tile<DT, OUT, T256x128>(g, s, kname, "sp24_big_256x128");
-        return launch_tile<DT, OUT, T128x128>(g, s, kname, "sp24_big_128x128");
+        // 128 x 128 tiles while they alone keep most CUs busy; fewer, the
+        // 128 x 64 ones (measured: 14-19% faster at 128 tiles of 128 x 128)
+        if (tiles_of<T128x128>(g) / T128x128::OCC >= kFill)
+            return launch_tile<DT, OUT, T128x128>(g, s, kname, "sp24_big_128x128");
+        return launch_tile<DT, OUT, T128x64>(g, s, kname, "sp24_big_128x64");
     }
     if (tiles_of<T256x64>(g) >= kFill) return launch_tile<DT, OUT, T256x64>(g, s, kname, "sp24_big_256x64");
     return launch_tile<DT, OUT, T128x64>(g, s, kname, "sp24_big_128x64");
@@ -541,7 +545,9 @@ hipError_t launch_hybrid(const HybridArgs& h, hipStream_t s, const char** kname)
             return launch_hybrid_tile<DT, OUT, T256x256>(h, s, kname, "sp24_hybrid_256x256");
         if (t128 >= kFill)
             return launch_hybrid_tile<DT, OUT, T256x128>(h, s, kname, "sp24_hybrid_256x128");
-        return launch_hybrid_tile<DT, OUT, T128x128>(h, s, kname, "sp24_hybrid_128x128");
+        if (hybrid_tiles_of<T128x128>(h) / T128x128::OCC >= kFill)
+            return launch_hybrid_tile<DT, OUT, T128x128>(h, s, kname, "sp24_hybrid_128x128");
+        return launch_hybrid_tile<DT, OUT, T128x64>(h, s, kname, "sp24_hybrid_128x64");
     }
     if (hybrid_tiles_of<T256x64>(h) >= kFill)
         return launch_hybrid_tile<DT, OUT, T256x64>(h, s, kname, "sp24_hybrid_256x64");

@@ -144,10 +144,12 @@ def test_gemm_kernel_names_follow_the_dispatch():
     assert k(False, sp.SPARSE_W, bf, bf, 2048, 5120, 4096) == "dense_big_256x256"
     assert k(True, sp.SPARSE_W, bf, bf, 2048, 4096, 4096) == "sp24_big_256x128"
     assert k(True, sp.SPARSE_W, bf, bf, 2048, 4096, 4096) == "sp24_big_256x128"
-    assert k(True, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "sp24_big_128x128"
+    assert k(True, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "sp24_big_128x64"        # 128 tiles of 128x128: fewer than 192
+    assert k(True, sp.SPARSE_W, bf, bf, 1024, 4096, 4096) == "sp24_big_128x128"
     assert k(True, sp.SPARSE_W, bf, bf, 64, 28672, 4096) == "sp24_big_128x64"
     assert k(False, sp.SPARSE_W, bf, bf, 8192, 4096, 4096) == "dense_big_256x256"
-    assert k(False, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "dense_big_128x128"
+    assert k(False, sp.SPARSE_W, bf, bf, 512, 4096, 4096) == "dense_big_128x64"
+    assert k(False, sp.SPARSE_W, bf, bf, 1024, 4096, 4096) == "dense_big_128x128"
     assert k(False, sp.SPARSE_W, bf, bf, 64, 28672, 4096) == "dense_big_128x64"
     # rejected shapes and degenerate ones
     assert k(True, sp.SPARSE_W, bf, bf, 4, 4096, 96) is None
@@ -282,7 +284,8 @@ def test_hybrid_validation_precedes_hip():
     assert k(bf, bf, 1536, 2048, 1024, 4096) == "sp24_hybrid_256x128"
     assert k(bf, bf, 64, 4096, 512, 4096) == "sp24_hybrid_128x64"
     assert k(bf, bf, 64, 49152, 512, 4096) == "sp24_hybrid_256x64"
-    assert k(bf, bf, 512, 512, 256, 4096) == "sp24_hybrid_128x128"
+    assert k(bf, bf, 512, 512, 256, 4096) == "sp24_hybrid_128x64"
+    assert k(bf, bf, 1000, 2048, 768, 4096) == "sp24_hybrid_128x128"
     assert k(bf, bf, 0, 16, 8, 64) == "none" and k(bf, bf, 4, 16, 8, 0) == "fill_zero"
     assert k(bf, bf, 4, 12, 8, 64) is None and k(bf, bf, 4, 16, 8, 96) is None
 

@@ -194,13 +194,14 @@ def test_dense_accepts_k_the_sparse_path_rejects(dt, M, N, K):
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
 @pytest.mark.parametrize("which", ["sparse_w", "sparse_x", "dense"])
 @pytest.mark.parametrize("steps", [6, 7])
-@pytest.mark.parametrize("MN", [(3000, 4100), (3000, 3000), (600, 1000)])
+@pytest.mark.parametrize("MN", [(3000, 4100), (3000, 3000), (2000, 4000), (1500, 2040), (600, 1000)])
 def test_large_tile_kernels_ragged(dt, which, steps, MN):
-    """The LDS-staged tile kernels (sparse 256x256, 256x128, 128x128; dense
-    256x256 and 128x128) on ragged last tiles in both dimensions (and, for
-    dense, a partial last K step), with an even and an odd count of K steps
-    (the sparse kernels load metadata two 16-bit steps at a time).  Integer
-    inputs: sampled rows must match the oracle exactly."""
+    """The LDS-staged tile kernels (256x256, 256x128, 128x128 and 128x64,
+    sparse and dense, by the tile rule on these shapes) on ragged last tiles
+    in both dimensions (and, for dense, a partial last K step), with an even
+    and an odd count of K steps (the sparse kernels load metadata in blocks of
+    four 16-bit or two fp8 steps).  Integer inputs: sampled rows must match
+    the oracle exactly."""
     M, N = MN
     K = steps * (64 if dt != oracle.E4M3 else 128)
     if which == "dense":

@@ -59,6 +59,7 @@ CASES = [
     (oracle.BF16, oracle.BF16, 64, 12288, 1000, 256),
     (oracle.BF16, oracle.BF16, 48, 49152, 520, 128),
     (oracle.BF16, oracle.BF16, 1536, 2048, 1024, 512),
+    (oracle.BF16, oracle.BF16, 1000, 2048, 768, 512),
     (oracle.BF16, oracle.BF16, 2048, 4096, 1024, 256),
     (oracle.BF16, oracle.BF16, 200, 0, 776, 320),
     (oracle.F16, oracle.F16, 130, 648, 0, 256),
