@@ -29,8 +29,10 @@
 //     16-byte chunks of a row are XOR-swizzled by row so that the fragment
 //     reads (16 rows x 16 B per lane group) hit 16 distinct bank groups;
 //   - workgroups are ordered so that the ones resident on one XCD at a time
-//     form a 4 (A tiles) x 8 (B tiles) block that shares operands through
-//     that XCD's L2.
+//     (32) form an 8 (A tiles) x 4 (B tiles) block that shares operands
+//     through that XCD's L2;
+//   - a grid whose last round would leave most of the chip idle runs that
+//     round as quarter tiles (sp24_big_tail).
 #include "mfma_ops.h"
 
 namespace sp24 {
