@@ -446,12 +446,21 @@ def main():
             db = dense_gemm_bytes(M, N, K, eb, out_eb, scales)
             fl = 2.0 * M * N * K
             tsm, tdm = float(np.median(ts)), float(np.median(td))
+            # dense-equivalent MFMA peak of the case (the hybrid's dense rows run at the dense rate)
+            case_peak = SPARSE_PEAK_TFLOPS[dt] if workload != HYBRID else \
+                (c["NS"] + c["ND"]) / (c["NS"] / SPARSE_PEAK_TFLOPS[dt] + c["ND"] / DENSE_PEAK_TFLOPS[dt])
             row = {"N": N, "K": K, "M": M, "t_sparse_us": round(tsm, 2), "t_dense_us": round(tdm, 2),
                    "speedup": round(tdm / tsm, 3),
                    "sparse_tflops": round(fl / tsm / 1e6, 1), "dense_tflops": round(fl / tdm / 1e6, 1),
                    "sparse_GBps": round(sb / tsm / 1e3, 1), "dense_GBps": round(db / tdm / 1e3, 1),
                    "sparse_hbm_frac": round(sb / tsm / 1e3 / HBM_PEAK_GBPS, 3),
-                   "sparse_mfma_frac": round(fl / tsm / 1e6 / SPARSE_PEAK_TFLOPS[dt], 3)}
+                   "sparse_mfma_frac": round(fl / tsm / 1e6 / SPARSE_PEAK_TFLOPS[dt], 3),
+                   # the case's own roofline: min(MFMA peak, arithmetic intensity x HBM peak), which at
+                   # the ridge (prefill M = 512) is below both peaks
+                   "sparse_attainable_frac": round(
+                       (fl / tsm / 1e6) / min(case_peak, fl / sb * HBM_PEAK_GBPS / 1e3), 3),
+                   "t_sparse_p10_us": round(float(np.percentile(ts, 10)), 2),
+                   "t_sparse_p90_us": round(float(np.percentile(ts, 90)), 2)}
             if workload == HYBRID:
                 tsp = float(np.median(times[("split",) + key]))
                 row.update(N_s=c["NS"], N_d=c["ND"], t_two_launch_us=round(tsp, 2),
@@ -531,6 +540,23 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic_per_launch(kname, workload),
                 "kernel": kname, "launches": k["n"], "flops_per_launch": round(k["flops"] / k["n"]),
                 "bytes_per_launch": round(k["bytes"] / k["n"]), "avg_launch_us": round(avg_us, 3)}
+    if hbm_bound:
+        # the same figure against a bandwidth this part reaches: an elementwise negation over 512 MiB
+        # (reads and writes 512 MiB), timed after the measured steps
+        a = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(2):
+            torch.neg(a, out=b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            torch.neg(a, out=b)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * a.numel() * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del a, b
+        roof["measured_copy_GBps"] = round(copy_gbps, 1)
+        roof["frac_of_measured_copy"] = round(achieved / copy_gbps, 4)
     all_t = sum(v["t"] for v in per_kernel.values())
     roof["kernels"] = {n: {"launches": v["n"], "avg_launch_us": round(v["t"] / v["n"], 3),
                            "share": round(v["t"] / all_t, 3)} for n, v in per_kernel.items()}
