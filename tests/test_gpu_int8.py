@@ -35,9 +35,11 @@ def test_prune_compress_and_decompress_bytewise(rows, K):
     assert np.array_equal(to_host(back, I8), oracle.decompress(I8, v, m, K))
 
 
-# decode kernels (M <= 64), tile kernels (M = 512; M = 4096 on sampled rows)
+# decode kernels (M <= 64, with 32-row tiles on the wide ones), tile kernels (M = 512; larger M on
+# sampled rows), including the 128x128 tiles and the quarter-tile tail of a 320-tile grid
 GEMM = [(1, 4096, 1024), (4, 1000, 512), (8, 8192, 512), (16, 2048, 1024), (24, 1024, 512), (33, 640, 512),
-        (64, 768, 2048), (512, 1536, 1024), (4096, 2048, 512), (2048, 6144, 256)]
+        (64, 768, 2048), (512, 1536, 1024), (4096, 2048, 512), (2048, 6144, 256),
+        (24, 6150, 512), (48, 5200, 512), (1024, 3072, 512), (4096, 5120, 512)]
 
 
 def _operands(M, N, K, seed):
