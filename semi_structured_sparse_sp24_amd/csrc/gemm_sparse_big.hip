@@ -435,6 +435,47 @@ sp24_hybrid(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, con
     }
 }
 
+// The hybrid grid with a short last round, split as sp24_big_tail splits the
+// plain one: the first n_big tiles (compressed, then dense, as in
+// sp24_hybrid) whole, each later one as four quarter tiles of its region
+// (a dense quarter: 64 dense rows x 128 rows of B).
+template <sp24_dtype DT, sp24_dtype OUT>
+__global__ void __launch_bounds__(T256x256::THREADS, 1)
+sp24_hybrid_tail(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const uint8_t* __restrict__ ad,
+                 const uint8_t* __restrict__ B, const float* __restrict__ sa, const float* __restrict__ sd,
+                 const float* __restrict__ sb, void* __restrict__ Y, void* __restrict__ Yd, int RS, int RD, int RB,
+                 int64_t K, int64_t sya, int64_t syb, int tiles_s, int tiles_d, int tiles_b, int n_big) {
+    SP24_TILE_LDS(T256x256);
+    const int b = (int)blockIdx.x, ns = tiles_s * tiles_b;
+    int t = 0, q = -1;   // tile, and the quarter of it (-1: whole)
+    if (b < n_big) {
+        t = xcd_order_of(b, n_big);
+    } else {
+        // n_big is a multiple of 8, so b - n_big keeps b's XCD
+        const int qq = xcd_order_of(b - n_big, (int)gridDim.x - n_big);
+        t = n_big + qq / 4;
+        q = qq & 3;
+    }
+    const int qa = (q >> 1) & 1, qb = q & 1;
+    if (t < ns) {
+        const TilePos p = tile_pos(t, tiles_s, tiles_b);
+        if (q < 0)
+            tile_body<DT, OUT, T256x256, false>(asb, bsb, msb, av, am, B, sa, sb, Y, RS, RB, K, sya, syb,
+                                                p.ta * 256, p.tb * 256, p.group);
+        else
+            tile_body<DT, OUT, T128x128, false>(asb, bsb, msb, av, am, B, sa, sb, Y, RS, RB, K, sya, syb,
+                                                p.ta * 256 + 128 * qa, p.tb * 256 + 128 * qb, p.group);
+    } else {
+        const TilePos p = tile_pos(t - ns, tiles_d, tiles_b);
+        if (q < 0)
+            tile_body<DT, OUT, T256x256, true>(asb, bsb, msb, ad, nullptr, B, sd, sb, Yd, RD, RB, K, sya, syb,
+                                               p.ta * 128, p.tb * 256, p.group);
+        else
+            tile_body<DT, OUT, T128x128, true>(asb, bsb, msb, ad, nullptr, B, sd, sb, Yd, RD, RB, K, sya, syb,
+                                               p.ta * 128 + 64 * qa, p.tb * 256 + 128 * qb, p.group);
+    }
+}
+
 template <sp24_dtype DT, sp24_dtype OUT, class TL>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s, const char** kname, const char* name) {
     const int RA = (int)(g.a_is_w ? g.N : g.M);
@@ -530,6 +571,23 @@ hipError_t launch_hybrid_tile(const HybridArgs& h, hipStream_t s, const char** k
     return hipGetLastError();
 }
 
+template <sp24_dtype DT, sp24_dtype OUT>
+hipError_t launch_hybrid_tail(const HybridArgs& h, hipStream_t s, const char** kname, int64_t n_big,
+                              int64_t n_split) {
+    const int RS = (int)h.NS, RD = (int)h.ND, RB = (int)h.M;
+    const int tiles_s = (RS + 255) / 256, tiles_d = (RD + 127) / 128, tiles_b = (RB + 255) / 256;
+    if (kname)
+        *kname = "sp24_hybrid_256x256_tail";
+    if (h.dry)
+        return hipSuccess;
+    void* Yd = (uint8_t*)h.Y + h.NS * elem_bytes(OUT);
+    hipLaunchKernelGGL((sp24_hybrid_tail<DT, OUT>), dim3((unsigned)(n_big + 4 * n_split)), dim3(T256x256::THREADS), 0,
+                       s, (const uint8_t*)h.ws_vals, h.ws_meta, (const uint8_t*)h.wd, (const uint8_t*)h.x, h.scale_w,
+                       h.scale_w ? h.scale_w + h.NS : nullptr, h.scale_x, h.Y, Yd, RS, RD, RB, h.K, (int64_t)1,
+                       h.NS + h.ND, tiles_s, tiles_d, tiles_b, (int)n_big);
+    return hipGetLastError();
+}
+
 template <class TL>
 int64_t hybrid_tiles_of(const HybridArgs& h) {
     const int64_t ts = (h.NS + TL::BA - 1) / TL::BA, td = (h.ND + TL::BA / 2 - 1) / (TL::BA / 2);
@@ -543,6 +601,9 @@ hipError_t launch_hybrid(const HybridArgs& h, hipStream_t s, const char** kname)
     constexpr int64_t kCUs = 256;
     if (h.M > 64) {
         const int64_t t256 = hybrid_tiles_of<T256x256>(h), t128 = hybrid_tiles_of<T256x128>(h);
+        const int64_t rest = t256 % kCUs;
+        if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs)
+            return launch_hybrid_tail<DT, OUT>(h, s, kname, t256 - rest, rest);
         if (t256 >= kFill || (t128 >= kFill && prefer_256(t256, t128, kCUs)))
             return launch_hybrid_tile<DT, OUT, T256x256>(h, s, kname, "sp24_hybrid_256x256");
         if (t128 >= kFill)

@@ -286,6 +286,7 @@ def test_hybrid_validation_precedes_hip():
     assert k(bf, bf, 64, 49152, 512, 4096) == "sp24_hybrid_256x64"
     assert k(bf, bf, 512, 512, 256, 4096) == "sp24_hybrid_128x64"
     assert k(bf, bf, 1000, 2048, 768, 4096) == "sp24_hybrid_128x128"
+    assert k(bf, bf, 2048, 4096, 2176, 4096) == "sp24_hybrid_256x256_tail"      # 264 = 256 + 8 tiles
     assert k(bf, bf, 0, 16, 8, 64) == "none" and k(bf, bf, 4, 16, 8, 0) == "fill_zero"
     assert k(bf, bf, 4, 12, 8, 64) is None and k(bf, bf, 4, 16, 8, 96) is None
 

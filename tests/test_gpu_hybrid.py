@@ -72,6 +72,27 @@ def test_hybrid_matches_oracle(dt, out, M, NS, ND, K):
     assert oracle.relative_error(Y, R) <= TOL[dt], name
 
 
+@pytest.mark.parametrize("M,NS,ND", [(2048, 4096, 2176), (2304 - 20, 7424, 128 - 8)])
+def test_hybrid_tail_quarter_tiles(M, NS, ND):
+    """A hybrid grid of 256x256 tiles just past one round (264 and 270
+    tiles): the remainder runs as quarter tiles, dense ones only in the first
+    case, compressed and dense in the second.  Integer operands: sampled rows
+    bitwise equal to the oracle, and every output written."""
+    K = 256
+    name = sp.hybrid_kernel(torch.bfloat16, torch.float32, M, NS, ND, K)
+    assert name == "sp24_hybrid_256x256_tail", name
+    x, wd, v, m, sx, sw = _operands(oracle.BF16, M, NS, ND, K, 11 + M, integer=True)
+    say("hybrid tail", M, NS, ND, K)
+    Y = torch.full((M, NS + ND), float("nan"), dtype=torch.float32, device="cuda")
+    sp.hybrid_gemm(to_dev(v, oracle.BF16), to_dev(m, oracle.F32), to_dev(wd, oracle.BF16), to_dev(x, oracle.BF16),
+                   NS, ND, out=Y)
+    torch.cuda.synchronize()
+    assert torch.isfinite(Y).all()
+    rows = np.unique(np.clip(np.concatenate([np.arange(0, M, 256), np.arange(129, M, 256), [M - 1]]), 0, M - 1))
+    R = oracle.hybrid_gemm(oracle.BF16, len(rows), NS, ND, K, x=x[rows], ws_vals=v, ws_meta=m, wd=wd)
+    assert np.array_equal(decode_out(Y)[rows], R)
+
+
 @pytest.mark.parametrize("M,NS,ND", [(260, 256, 136), (32, 512, 200)])
 def test_hybrid_fp8_with_scales(M, NS, ND):
     Y, R, name = _run(oracle.E4M3, oracle.BF16, M, NS, ND, 1024, 7 + M)
