@@ -232,7 +232,7 @@ def test_large_tile_kernels_ragged(dt, which, steps, MN):
 TAIL = [(4066, 4302, 6), (4096, 5120 - 40, 7), (1000, 68 * 256 - 7, 5)]
 
 
-@pytest.mark.parametrize("dt", [oracle.BF16, oracle.E4M3])
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
 @pytest.mark.parametrize("which", ["sparse_w", "sparse_x", "dense"])
 @pytest.mark.parametrize("M,N,steps", TAIL)
 def test_tail_quarter_tiles(dt, which, M, N, steps):
@@ -244,7 +244,7 @@ def test_tail_quarter_tiles(dt, which, M, N, steps):
     RA, RB = (M, N) if which == "sparse_x" else (N, M)
     t = ((RA + 255) // 256) * ((RB + 255) // 256)
     assert t > 256 and 0 < t % 256 <= 64, t
-    ttype = {oracle.BF16: torch.bfloat16, oracle.E4M3: torch.float8_e4m3fn}[dt]
+    ttype = {oracle.BF16: torch.bfloat16, oracle.F16: torch.float16, oracle.E4M3: torch.float8_e4m3fn}[dt]
     op = sp.SPARSE_X if which == "sparse_x" else sp.SPARSE_W
     name = "dense_big_256x256_tail" if which == "dense" else "sp24_big_256x256_tail"
     assert sp.gemm_kernel(which != "dense", op, ttype, torch.float32, M, N, K) == name
