@@ -506,7 +506,12 @@ SP24_API sp24_status sp24_select_tactic(sp24_operand which, sp24_dtype in_dt, sp
         return dense_impl(in_dt, out_dt, M, N, K, X, W, scale_x, scale_w, Y_scratch, stream, &dname);
     };
 
-    std::vector<hipEvent_t> ev((size_t)reps * 5, nullptr);
+    // per rep: sparse start, split (after compress), end; dense start, split, end.  The dense
+    // side records a split too, right at its start, so that both measurements hold the same
+    // number of event markers: a marker between two events is itself timed, and on small
+    // kernels one extra marker on one side only would bias the choice.
+    constexpr size_t kEv = 6;
+    std::vector<hipEvent_t> ev((size_t)reps * kEv, nullptr);
     sp24_status result = SP24_OK;
     for (auto& e : ev)
         if (hipEventCreate(&e) != hipSuccess) {
@@ -523,14 +528,17 @@ SP24_API sp24_status sp24_select_tactic(sp24_operand which, sp24_dtype in_dt, sp
         }
         // interleave the two paths rep by rep so that clock and thermal drift hit both
         for (int i = 0; i < reps && result == SP24_OK; ++i) {
-            hipEvent_t* e = &ev[(size_t)i * 5];
+            hipEvent_t* e = &ev[(size_t)i * kEv];
             if (eligible) {
                 if (hipEventRecord(e[0], stream) != hipSuccess) { result = SP24_E_HIP; break; }
                 result = run_sparse(e[1]);
                 if (result != SP24_OK) break;
                 if (hipEventRecord(e[2], stream) != hipSuccess) { result = SP24_E_HIP; break; }
             }
-            if (hipEventRecord(e[3], stream) != hipSuccess) { result = SP24_E_HIP; break; }
+            if (hipEventRecord(e[3], stream) != hipSuccess || hipEventRecord(e[5], stream) != hipSuccess) {
+                result = SP24_E_HIP;
+                break;
+            }
             result = run_dense();
             if (result != SP24_OK) break;
             if (hipEventRecord(e[4], stream) != hipSuccess) { result = SP24_E_HIP; break; }
@@ -538,7 +546,7 @@ SP24_API sp24_status sp24_select_tactic(sp24_operand which, sp24_dtype in_dt, sp
         if (result == SP24_OK && hipStreamSynchronize(stream) != hipSuccess)
             result = SP24_E_HIP;
         for (int i = 0; i < reps && result == SP24_OK; ++i) {
-            hipEvent_t* e = &ev[(size_t)i * 5];
+            hipEvent_t* e = &ev[(size_t)i * kEv];
             float a = 0.f, b = 0.f, c = 0.f;
             if (eligible) {
                 if (hipEventElapsedTime(&a, e[0], e[1]) != hipSuccess ||
