@@ -8,7 +8,8 @@
 //   skinny  few rows of X (<= 16, or <= 64 on a narrow output): the
 //           workgroup owns 16 rows of W and all of X; waves split K;
 //           v_mfma_f32_16x16x32 (16-bit, two per 64-K step) or
-//           v_mfma_scale_f32_16x16x128_f8f6f4 (fp8, unit scales);
+//           v_mfma_scale_f32_16x16x128_f8f6f4 (fp8, unit scales); 5 to 16
+//           rows of X staged in LDS as the sparse decode kernel does;
 //   tiles   everything else: the LDS-staged tile kernels of
 //           gemm_dense_big.hip.
 // D is computed with A = W (rows N) and B = X (rows M), i.e. the tile of
@@ -180,6 +181,124 @@ dense_skinny(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 5 to 16 rows of X: the construction of the sparse decode kernel for that
+// range.  Waves split K into groups of 8 steps; W goes straight into
+// registers; all 16 rows of X are staged in LDS, each row of a group one
+// contiguous 1 KiB load with its 16-byte chunks XOR-permuted by the row
+// number (16 rows read by one fragment load fall in 16 bank groups); AT
+// 16-row tiles of W per workgroup; WV waves; the staging area then holds the
+// cross-wave reduction.
+template <sp24_dtype DT, sp24_dtype OUT, int AT, int WV>
+__global__ void __launch_bounds__(WV * 64)
+dense_skinny_x16(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
+                 const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K) {
+    using Op = DenseOp16<DT>;
+    constexpr int STEP_BYTES = Op::KSTEP * Op::ELEM;   // 128
+    constexpr int G = 8;                               // K steps per load group
+    constexpr int X_ROW = G * STEP_BYTES;              // one row of X per group
+    static_assert(X_ROW == 1024, "one 1 KiB load per staged row and group");
+    constexpr int PER_WAVE = 16 * X_ROW;
+    static_assert(AT * 4 * 64 * 4 <= PER_WAVE, "the reduction fits in the staging area");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[WV * PER_WAVE];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, kg = lane >> 4;
+    const int n0 = blockIdx.x * 16 * AT;
+    const int steps = (int)((K + Op::KSTEP - 1) / Op::KSTEP);   // the last step may be partial
+    const int groups = (steps + G - 1) / G;
+    const uint32_t row_bytes = (uint32_t)(K * Op::ELEM);
+    const int o0 = 16 * kg, o1 = STEP_BYTES / 2 + 16 * kg;
+    const Buf bufW(W, (uint32_t)N * row_bytes);   // rows past N / M read as zeros
+    const Buf bufX(X, (uint32_t)M * row_bytes);
+    uint8_t* my_x = lds + wave * PER_WAVE;
+    const uint8_t* xr = my_x + X_ROW * r;
+    uint32_t a_base[AT];
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+        a_base[t] = (uint32_t)(n0 + 16 * t + r) * row_bytes;
+    f32x4 acc[AT];
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+        acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int per_wave = (groups + WV - 1) / WV;
+    const int rot = (int)((blockIdx.x * 5u) % (unsigned)max(groups, 1));
+    for (int gi = 0; gi < per_wave; ++gi) {
+        const int gl = wave * per_wave + gi;
+        if (gl >= groups)
+            break;
+        const int g = gl + rot >= groups ? gl + rot - groups : gl + rot;
+        const uint32_t k_first = (uint32_t)g * X_ROW;   // the group's first byte in a row
+        // W: 16-byte chunks past K (a partial last step, or steps past it) read as zeros
+        uint4 a0[AT][G], a1[AT][G];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const uint32_t k0 = k_first + (uint32_t)u * STEP_BYTES;
+            const bool in0 = k0 + o0 < row_bytes, in1 = k0 + o1 < row_bytes;
+#pragma unroll
+            for (int t = 0; t < AT; ++t) {
+                a0[t][u] = bufW.ld16(in0 ? a_base[t] + k0 + o0 : kOOB);
+                a1[t][u] = bufW.ld16(in1 ? a_base[t] + k0 + o1 : kOOB);
+            }
+        }
+        // X row j: lane l fetches the chunk that belongs in slot l, chunk l ^ j
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t col = k_first + 16 * (lane ^ j);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufX.r, (lds_void*)(my_x + X_ROW * j), 16,
+                                                     (int)(col < row_bytes ? (uint32_t)j * row_bytes + col : kOOB),
+                                                     0, 0, 0);
+        }
+        // this wave's loads have landed
+        __builtin_amdgcn_s_waitcnt((0) | (0x7 << 4) | (0xF << 8));
+        // steps past the end of K run on zeros and add nothing
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const uint4 b0 = *reinterpret_cast<const uint4*>(xr + 16 * ((8 * u + o0 / 16) ^ r));
+            const uint4 b1 = *reinterpret_cast<const uint4*>(xr + 16 * ((8 * u + o1 / 16) ^ r));
+#pragma unroll
+            for (int t = 0; t < AT; ++t)
+                acc[t] = Op::mma(a0[t][u], a1[t][u], b0, b1, acc[t]);
+        }
+        // the next group's loads reuse this wave's LDS: finish reading it
+        __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
+    }
+
+    // every wave is past its staging area before it holds the partial tiles
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);   // [WV][AT][4][64]
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            red[((wave * AT + t) * 4 + i) * 64 + lane] = acc[t][i];
+    __syncthreads();
+    for (int o = threadIdx.x; o < AT * 256; o += WV * 64) {
+        const int t = o >> 8, ot = o & 255;
+        const int al = ot & 15, bl = ot >> 4;
+        const int ln = ((al >> 2) << 4) | bl, i = al & 3;
+        float v = 0.f;
+        if constexpr (DT == SP24_I8) {
+            int vi = 0;
+            for (int w = 0; w < WV; ++w)
+                vi += __builtin_bit_cast(int, red[((w * AT + t) * 4 + i) * 64 + ln]);
+            v = (float)vi;
+        } else {
+            for (int w = 0; w < WV; ++w)   // fixed order: deterministic
+                v += red[((w * AT + t) * 4 + i) * 64 + ln];
+        }
+        const int n = n0 + 16 * t + al, m = bl;
+        if (n < N && m < M) {
+            if (sx)
+                v *= sx[m];
+            if (sw)
+                v *= sw[n];
+            store_out<OUT>(Y, (int64_t)m * N + n, v);
+        }
+    }
+}
+
 template <sp24_dtype DT, sp24_dtype OUT>
 hipError_t dispatch(const DenseArgs& g, hipStream_t s, const char** kname) {
     const int N = (int)g.N, M = (int)g.M;
@@ -206,7 +325,34 @@ hipError_t dispatch(const DenseArgs& g, hipStream_t s, const char** kname) {
         // 17 to 64 rows of X: 32-row W tiles when that still leaves 160 or more
         // workgroups (each X fragment then serves two W tiles), as the sparse
         // decode kernel does
-        if (mt <= 1) DENSE_SKINNY(1, 4, 1, "dense_skinny_m1");
+        // 5 to 16 rows: staged in LDS, with the sparse decode kernel's choice
+        // of waves and of 32-row W tiles
+        if (mt <= 1 && M > 4) {
+            const int groups = (steps + 7) / 8;
+            int wv = 8;
+            while (wv > 2 && groups < wv)
+                wv >>= 1;
+            const bool at2 = tiles16 / 2 >= 192;
+            if (at2 && tiles16 / 2 >= 3 * 256)
+                wv = min(wv, 4);
+#define DENSE_X16(AT, NAME)                                                                          \
+    do {                                                                                             \
+        const dim3 grid((N + 16 * AT - 1) / (16 * AT));                                              \
+        if (!g.dry) {                                                                                \
+            if (wv <= 4)                                                                             \
+                hipLaunchKernelGGL((dense_skinny_x16<DT, OUT, AT, 4>), grid, dim3(256), 0, s, W, X,  \
+                                   g.scale_x, g.scale_w, g.Y, N, M, g.K);                            \
+            else                                                                                     \
+                hipLaunchKernelGGL((dense_skinny_x16<DT, OUT, AT, 8>), grid, dim3(512), 0, s, W, X,  \
+                                   g.scale_x, g.scale_w, g.Y, N, M, g.K);                            \
+        }                                                                                            \
+        if (kname) *kname = NAME;                                                                    \
+    } while (0)
+            if (at2) DENSE_X16(2, "dense_skinny_m16_a32");
+            else DENSE_X16(1, "dense_skinny_m16");
+#undef DENSE_X16
+        }
+        else if (mt <= 1) DENSE_SKINNY(1, 4, 1, "dense_skinny_m1");
         else if (mt == 2 && a32) DENSE_SKINNY(2, 2, 2, "dense_skinny_m2_a32");
         else if (mt == 2) DENSE_SKINNY(2, 2, 1, "dense_skinny_m2");
         else if (a32) DENSE_SKINNY(4, 2, 2, "dense_skinny_m4_a32");

@@ -16,6 +16,7 @@
 //           of a group at once (A into registers, metadata and up to 4 B rows
 //           into LDS by direct global->LDS loads), and reduce their partial
 //           tiles through LDS in a fixed order (deterministic, no atomics).
+//           5 to 16 B rows: sp24_skinny_x16, the same with all 16 rows staged.
 // Larger B goes to the LDS-staged tile kernels of gemm_sparse_big.hip.
 #include "mfma_ops.h"
 
@@ -227,6 +228,152 @@ sp24_skinny(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
     }
 }
 
+// 5 to 16 dense rows: the plan above with all 16 rows of B staged in LDS.
+// In registers, a B fragment puts 16 different rows in every 16 lanes, so
+// each lane's 16 bytes is a request of its own to L2; staged, each row of the
+// group is one contiguous 1 KiB load (8 whole lines).  The 16-byte chunks of
+// a staged row are XOR-permuted by the row number, so that the 16 rows read
+// by one fragment load fall in 16 different bank groups.  After the K loop
+// the staging area holds the cross-wave reduction.  WV: waves per workgroup.
+template <sp24_dtype DT, sp24_dtype OUT, int AT, int WV>
+__global__ void __launch_bounds__(WV * 64)
+sp24_skinny_x16(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
+                const uint8_t* __restrict__ B, const float* __restrict__ sa, const float* __restrict__ sb,
+                void* __restrict__ Y, int RA, int RB, int64_t K, int64_t sya, int64_t syb) {
+    using L = StepLayout<DT>;
+    using Op = SparseOp<DT>;
+    constexpr int MWS = L::META_WORDS;
+    constexpr int M_ROW = kGroup * MWS * 4;         // metadata bytes of one row per group: 64 or 128
+    constexpr int M_CPR = M_ROW / 16;               // 16-byte chunks per row: 4 or 8
+    constexpr int META = 16 * AT * M_ROW;           // metadata of the group's 16 * AT rows
+    constexpr int M_LOADS = META / 1024;
+    constexpr int M_RPL = 1024 / M_ROW;             // rows per load: 16 or 8
+    constexpr int X_ROW = kGroup * L::B_STEP_BYTES; // one B row of the group
+    static_assert(X_ROW == 1024, "one 1 KiB load per staged row and group");
+    constexpr int PER_WAVE = META + 16 * X_ROW;
+    static_assert(AT * 4 * 64 * 4 <= PER_WAVE, "the reduction fits in the staging area");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[WV * PER_WAVE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, kg = lane >> 4;
+    const int a0 = blockIdx.x * 16 * AT;
+    const int steps = (int)(K / L::KSTEP);
+    const int groups = (steps + kGroup - 1) / kGroup;
+    const uint32_t a_row_bytes = (uint32_t)(K / 2 * L::ELEM), b_row_bytes = (uint32_t)(K * L::ELEM);
+    const uint32_t m_row_bytes = (uint32_t)(K / 8);
+    const Buf bufA(av, (uint32_t)RA * a_row_bytes);   // rows past RA / RB read as zeros
+    const Buf bufM(am, (uint32_t)RA * m_row_bytes);
+    const Buf bufB(B, (uint32_t)RB * b_row_bytes);
+    uint8_t* my_m = lds + wave * PER_WAVE;
+    uint8_t* my_x = my_m + META;
+
+    uint32_t a_base[AT];
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+        a_base[t] = (uint32_t)(a0 + 16 * t + r) * a_row_bytes + L::a_off(kg);
+    const int m_swz_r = M_CPR == 4 ? (r >> 2) & 3 : (r >> 1) & 7;
+    const int msh = L::meta_shift(kg), mwd = L::meta_word(kg);
+    // this lane's B row in LDS and its two chunks of step 0 (before the permutation)
+    const uint8_t* xr = my_x + X_ROW * r;
+    const int xc0 = L::b_off0(kg) / 16, xc1 = L::b_off1(kg) / 16;
+
+    f32x4 acc[AT];
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+        acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int per_wave = (groups + WV - 1) / WV;
+    const int rot = (int)((blockIdx.x * 5u) % (unsigned)max(groups, 1));
+    for (int gi = 0; gi < per_wave; ++gi) {
+        const int gl = wave * per_wave + gi;
+        if (gl >= groups)
+            break;
+        const int g = gl + rot >= groups ? gl + rot - groups : gl + rot;
+        const int s_first = g * kGroup;
+        const int n_in = min(kGroup, steps - s_first);
+        uint4 fa[AT][kGroup];
+#pragma unroll
+        for (int t = 0; t < AT; ++t)
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u)
+                fa[t][u] = bufA.ld16(u < n_in ? a_base[t] + (uint32_t)(s_first + u) * L::A_STEP_BYTES : kOOB);
+#pragma unroll
+        for (int h = 0; h < M_LOADS; ++h) {
+            const int row = h * M_RPL + lane / M_CPR;
+            const int swz = M_CPR == 4 ? (row >> 2) & 3 : (row >> 1) & 7;
+            const uint32_t col = (uint32_t)g * M_ROW + 16 * ((lane % M_CPR) ^ swz);
+            const bool in = col < m_row_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufM.r, (lds_void*)(my_m + 1024 * h), 16,
+                                                     (int)(in ? (uint32_t)(a0 + row) * m_row_bytes + col : kOOB),
+                                                     0, 0, 0);
+        }
+        // B row j: lane l fetches the chunk that belongs in slot l, chunk l ^ j
+        // (rows past RB and steps past K load zeros)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t col = (uint32_t)s_first * L::B_STEP_BYTES + 16 * (lane ^ j);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufB.r, (lds_void*)(my_x + X_ROW * j), 16,
+                                                     (int)(col < b_row_bytes ? (uint32_t)j * b_row_bytes + col : kOOB),
+                                                     0, 0, 0);
+        }
+        // this wave's loads have landed
+        __builtin_amdgcn_s_waitcnt((0) | (0x7 << 4) | (0xF << 8));
+        // steps past the end of K run on zeros (see sp24_skinny)
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const int wbyte = 4 * (MWS * u + mwd);
+            uint32_t idx[AT];
+#pragma unroll
+            for (int t = 0; t < AT; ++t)
+                idx[t] = *reinterpret_cast<const uint32_t*>(my_m + M_ROW * (16 * t + r) +
+                                                            16 * ((wbyte >> 4) ^ m_swz_r) + (wbyte & 15)) >> msh;
+            const uint4 b0 = *reinterpret_cast<const uint4*>(xr + 16 * ((8 * u + xc0) ^ r));
+            const uint4 b1 = *reinterpret_cast<const uint4*>(xr + 16 * ((8 * u + xc1) ^ r));
+#pragma unroll
+            for (int t = 0; t < AT; ++t)
+                acc[t] = Op::mma(fa[t][u], b0, b1, idx[t], acc[t]);
+        }
+        // the next group's loads reuse this wave's LDS: finish reading it
+        __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
+    }
+
+    // every wave is past its staging area before it holds the partial tiles
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);   // [WV][AT][4][64]
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            red[((wave * AT + t) * 4 + i) * 64 + lane] = acc[t][i];
+    __syncthreads();
+
+    // D[4*kg + i][l % 16] of tile t lives at red[.][t][i][kg*16 + l%16]
+    for (int o = threadIdx.x; o < AT * 256; o += WV * 64) {
+        const int t = o >> 8, ot = o & 255;
+        const int al = ot & 15, bl = ot >> 4;
+        const int ln = ((al >> 2) << 4) | bl, i = al & 3;
+        float v = 0.f;
+        if constexpr (DT == SP24_I8) {
+            int vi = 0;
+            for (int w = 0; w < WV; ++w)
+                vi += __builtin_bit_cast(int, red[((w * AT + t) * 4 + i) * 64 + ln]);
+            v = (float)vi;
+        } else {
+            for (int w = 0; w < WV; ++w)   // fixed order: deterministic
+                v += red[((w * AT + t) * 4 + i) * 64 + ln];
+        }
+        const int ar = a0 + 16 * t + al, br = bl;
+        if (ar < RA && br < RB) {
+            if (sa)
+                v *= sa[ar];
+            if (sb)
+                v *= sb[br];
+            store_out<OUT>(Y, (int64_t)ar * sya + (int64_t)br * syb, v);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ dispatch
 template <sp24_dtype DT, sp24_dtype OUT>
 hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
@@ -255,6 +402,21 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
                                g.K, sya, syb);                                                        \
         if (kname) *kname = NAME;                                                                     \
     } while (0)
+        // 5 to 16 rows: the kernel that stages all 16 (4 or 8 waves; fewer
+        // load groups than waves leave the extra waves idle)
+#define SP24_X16(AT, NAME)                                                                            \
+    do {                                                                                              \
+        const dim3 grid((RA + 16 * AT - 1) / (16 * AT));                                              \
+        if (!g.dry) {                                                                                 \
+            if (waves <= 4)                                                                           \
+                hipLaunchKernelGGL((sp24_skinny_x16<DT, OUT, AT, 4>), grid, dim3(256), 0, s, av, g.a_meta, b, \
+                                   g.scale_a, g.scale_b, g.Y, RA, RB, g.K, sya, syb);                 \
+            else                                                                                      \
+                hipLaunchKernelGGL((sp24_skinny_x16<DT, OUT, AT, 8>), grid, dim3(512), 0, s, av, g.a_meta, b, \
+                                   g.scale_a, g.scale_b, g.Y, RA, RB, g.K, sya, syb);                 \
+        }                                                                                             \
+        if (kname) *kname = NAME;                                                                     \
+    } while (0)
         // at most 4 dense rows: stage them through LDS with contiguous 1 KiB
         // loads (a register load per step carries 64 useful bytes of 1 KiB).
         // 5 to 16: 32 rows of A per workgroup when that still leaves 192 or
@@ -265,9 +427,9 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
             // three or more workgroups per CU: four waves each hold enough in flight
             if (tiles16 / 2 >= 3 * 256 && waves > 4)
                 waves = 4;
-            SP24_SKINNY(1, false, 2, 1, "sp24_skinny_m16_a32");
+            SP24_X16(2, "sp24_skinny_m16_a32");
         }
-        else if (mt <= 1) SP24_SKINNY(1, false, 1, 1, "sp24_skinny_m16");
+        else if (mt <= 1) SP24_X16(1, "sp24_skinny_m16");
         // 17 to 64: 32-row A tiles from 160 such tiles on (measured on the fp8
         // 5120-row and bf16 6144-row layers: 27-40% faster; on 4096 rows,
         // 128 tiles, 10-20% slower)
@@ -276,6 +438,7 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s, const char** kname) {
         else if (tiles16 / 2 >= 160) SP24_SKINNY(2, false, 2, 2, "sp24_skinny_m64_a32");
         else SP24_SKINNY(2, false, 1, 2, "sp24_skinny_m64");
 #undef SP24_SKINNY
+#undef SP24_X16
     } else {
         // the LDS-staged tile kernels, which read each B fragment once per
         // 128 or 256 rows of A

@@ -117,7 +117,8 @@ def test_quantize_validation_precedes_hip():
 def test_gemm_kernel_names_follow_the_dispatch():
     bf = __import__("torch").bfloat16
     k = sp.gemm_kernel
-    # decode: one to four dense rows are staged through LDS, up to 64 go through registers
+    # decode: up to four dense rows are staged through LDS, five to 16 as 16 staged rows,
+    # up to 64 go through registers
     assert k(True, sp.SPARSE_W, bf, bf, 1, 4096, 4096) == "sp24_skinny_x4"
     assert k(True, sp.SPARSE_W, bf, bf, 4, 4096, 4096) == "sp24_skinny_x4"
     assert k(True, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "sp24_skinny_m16"
@@ -128,7 +129,7 @@ def test_gemm_kernel_names_follow_the_dispatch():
     assert k(True, sp.SPARSE_W, bf, bf, 32, 5104, 4096) == "sp24_skinny_m32"
     assert k(False, sp.SPARSE_W, bf, bf, 64, 6144, 4096) == "dense_skinny_m4_a32"
     assert k(False, sp.SPARSE_W, bf, bf, 32, 5120, 4096) == "dense_skinny_m2_a32"
-    assert k(False, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "dense_skinny_m1"
+    assert k(False, sp.SPARSE_W, bf, bf, 16, 4096, 4096) == "dense_skinny_m16"
     # beyond 16 rows: the largest LDS-staged tile that still fills the chip
     assert k(True, sp.SPARSE_W, bf, bf, 8192, 4096, 4096) == "sp24_big_256x256"
     # more than one round of 256x256 tiles, the last at most a quarter of the chip: quarter tiles

@@ -144,7 +144,11 @@ SKINNY = [(1, 100, 704, "sp24_skinny_x4"), (4, 6150, 704, "sp24_skinny_x4"),
           (40, 17000, 704, "sp24_big_128x64"), (17, 61500, 192, "sp24_big_256x64"),
           # 32-row A tiles for 17 to 64 rows once there are 160 or more of them
           (30, 6150, 704, "sp24_skinny_m32_a32"), (64, 5200, 704, "sp24_skinny_m64_a32"),
-          (50, 5130, 192, "sp24_skinny_m64_a32")]
+          (50, 5130, 192, "sp24_skinny_m64_a32"),
+          # 5 to 16 rows with eight waves (nine or more load groups of K),
+          # a partial last group, and all 16 staged rows of B in use or not
+          (12, 3000, 4160, "sp24_skinny_m16"), (16, 6150, 4096, "sp24_skinny_m16_a32"),
+          (13, 24600, 4160, "sp24_skinny_m16_a32")]
 
 
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
@@ -162,7 +166,10 @@ def test_skinny_variants_exact(dt, M, N, K, kernel):
 
 DENSE_FEW = [(40, 17000, 704, "dense_big_128x64"), (17, 61500, 200, "dense_big_256x64"),
              (64, 190, 704, "dense_skinny_m4"), (20, 300, 200, "dense_skinny_m2"),
-             (64, 5200, 704, "dense_skinny_m4_a32"), (20, 6150, 200, "dense_skinny_m2_a32")]
+             (64, 5200, 704, "dense_skinny_m4_a32"), (20, 6150, 200, "dense_skinny_m2_a32"),
+             # 5 to 16 rows staged in LDS: partial last step, eight waves, 32-row tiles
+             (9, 300, 200, "dense_skinny_m16"), (12, 3000, 4160, "dense_skinny_m16"),
+             (16, 6150, 4096, "dense_skinny_m16_a32"), (13, 24600, 4168, "dense_skinny_m16_a32")]
 
 
 @pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16, oracle.E4M3])
