@@ -208,6 +208,72 @@ __device__ __forceinline__ void dense_tile(uint8_t* a0s, uint8_t* a1s, uint8_t* 
     wait_vmcnt_lgkm0<0>();
 
     // ---- epilogue: D[8*(v/4) + 4*kg + v%4][r] of fragment (i, j); a = W row (n), b = X row (m)
+    auto value = [&](const f32x16& accf, int h, int n, float fsx) {
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v[q] = accf[4 * h + q] * fsx * (sw && n + q < N ? sw[n + q] : 1.f);
+        return v;
+    };
+    if constexpr (OUT != SP24_F32) {
+        // Y is X-row-major, so a lane's four consecutive outputs are 8 bytes
+        // of one row of Y and a store instruction writes 16-byte pieces of 32
+        // rows.  As in the sparse tile kernels, a whole block of the wave (EA
+        // rows of W x EB rows of X) is staged in the free stage memory, row m
+        // of Y as a run of EA outputs with its 16-byte chunks XOR-permuted by
+        // m, and written back as whole 16-byte pieces, CPR lanes per row.
+        constexpr int EA = 32 * kFA, EB = 32 * kFB;
+        constexpr int W_STG = EA * EB * 2;                    // staging bytes per wave
+        constexpr int PA = kBA * 128 / W_STG, PB = kBB * 128 / W_STG;   // waves per W / X stage
+        static_assert(2 * PA + 2 * PB >= TL::WAVES, "staging fits the stages");
+        constexpr int CPR = EA / 8;                           // 16-byte chunks per staged row
+        constexpr int CPP = 64 / CPR;                         // rows per wave-wide read
+        static_assert(CPR >= 4 && CPR <= 16 && EB % CPP == 0, "staged block shape");
+        const int n_w = a0 + wa * EA, m_w = b0 + wb * EB;
+        if ((N & 7) == 0 && ((uintptr_t)Y & 15) == 0) {
+            // every wave is done with the stages
+            __syncthreads();
+            if (n_w + EA <= N && m_w + EB <= M) {
+                const int w = wave;
+                uint8_t* stg = w < PA ? a0s + w * W_STG
+                             : w < 2 * PA ? a1s + (w - PA) * W_STG
+                             : w < 2 * PA + PB ? b0s + (w - 2 * PA) * W_STG
+                                               : b1s + (w - 2 * PA - PB) * W_STG;
+                auto slot = [](int ml, int c) { return 16 * (c ^ ((ml / (16 / CPR)) & (CPR - 1))); };
+#pragma unroll
+                for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+                    for (int j = 0; j < kFB; ++j) {
+                        const int ml = j * 32 + r;
+                        const float fsx = sx ? sx[m_w + ml] : 1.f;
+                        const f32x16 accf = acc_to_f32<DT>(acc[i][j]);
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) {
+                            const int nl = i * 32 + 8 * h + 4 * kg;
+                            const f32x4 v = value(accf, h, n_w + nl, fsx);
+                            uint16_t hv[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                hv[q] = OUT == SP24_BF16 ? f32_to_bf16_rne(v[q]) : f32_to_f16_rne(v[q]);
+                            *reinterpret_cast<uint2*>(stg + ml * (EA * 2) + slot(ml, nl >> 3) + 8 * ((nl >> 2) & 1)) =
+                                make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+                        }
+                    }
+                }
+                // this wave's LDS writes complete before it reads them back
+                __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
+                __builtin_amdgcn_wave_barrier();
+                uint16_t* const y = reinterpret_cast<uint16_t*>(Y);
+#pragma unroll
+                for (int pass = 0; pass < EB / CPP; ++pass) {
+                    const int ml = pass * CPP + lane / CPR, c = lane % CPR;
+                    const uint4 d = *reinterpret_cast<const uint4*>(stg + ml * (EA * 2) + slot(ml, c));
+                    *reinterpret_cast<uint4*>(y + (int64_t)(m_w + ml) * N + n_w + 8 * c) = d;
+                }
+                return;
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < kFA; ++i) {
 #pragma unroll
@@ -222,10 +288,7 @@ __device__ __forceinline__ void dense_tile(uint8_t* a0s, uint8_t* a1s, uint8_t* 
                 const int n = a0 + wa * 32 * kFA + i * 32 + 8 * h + 4 * kg;
                 if (n >= N)
                     continue;
-                f32x4 v;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    v[q] = accf[4 * h + q] * fsx * (sw && n + q < N ? sw[n + q] : 1.f);
+                const f32x4 v = value(accf, h, n, fsx);
                 const int64_t off = (int64_t)m * N + n;
                 if (n + 3 < N && (off & 3) == 0) {
                     store_out4<OUT>(Y, off, v);

@@ -321,6 +321,68 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
     wait_vmcnt<0>();   // drain the (useless) loads of steps past the end
 
     // ---- epilogue: fragment (i, j), lane -> D[a][b], a = .. + 4*kg + q, b = .. + r
+    auto value = [&](int i, int j, int ar, int br) {
+        f32x4 v = acc_to_f32<DT>(acc[i][j]);
+        const float fsb = sb ? sb[br] : 1.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v[q] *= (sa && ar + q < RA ? sa[ar + q] : 1.f) * fsb;
+        return v;
+    };
+    if constexpr (OUT != SP24_F32 && kFA >= 2) {
+        // When A indexes the output's contiguous dimension (sya == 1: the
+        // transposed store of a weight-compressed GEMM), a lane's fragment
+        // holds four consecutive outputs of one column b, so a store
+        // instruction writes 8-byte pieces of 16 columns.  A whole block of
+        // the wave (EA rows of A x EB of B) is instead staged in the free
+        // stage memory, column b as a run of EA outputs, and written back as
+        // whole 16-byte pieces, CPR lanes per column.  The 16-byte chunks of
+        // a staged column are XOR-permuted by the column, so that the 16
+        // columns one fragment writes fall in 16 different bank groups.  (Blocks
+        // of 16 rows of A gain nothing: their columns are 32-byte pieces anyway.)
+        constexpr int EA = 16 * kFA, EB = 16 * kFB;
+        constexpr int W_STG = EA * EB * 2;             // staging bytes per wave
+        constexpr int IN_B = 3 * kBStage / W_STG;      // waves staged in the B stages; the rest in the A stages
+        static_assert(kWaves <= IN_B || (kWaves - IN_B) * W_STG <= 3 * kAStage, "staging fits the stages");
+        constexpr int CPR = EA / 8;                    // 16-byte chunks per staged column
+        constexpr int CPP = 64 / CPR;                  // columns per wave-wide read
+        static_assert(CPR >= 4 && CPR <= 16 && EB % CPP == 0, "staged block shape");
+        const int a_w = a0 + wa * EA, b_w = b0 + wb * EB;
+        const bool stage_ok = sya == 1 && (syb & 7) == 0 && ((uintptr_t)Y & 15) == 0;
+        if (stage_ok) {
+            // every wave is done with the stages (its loads past the end have landed)
+            __syncthreads();
+            if (a_w + EA <= RA && b_w + EB <= RB) {
+                uint8_t* stg = wave < IN_B ? bsb + wave * W_STG : asb + (wave - IN_B) * W_STG;
+                auto slot = [](int bl, int c) { return 16 * (c ^ ((bl / (16 / CPR)) & (CPR - 1))); };
+#pragma unroll
+                for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+                    for (int j = 0; j < kFB; ++j) {
+                        const int al = i * 16 + 4 * kg, bl = j * 16 + r;
+                        const f32x4 v = value(i, j, a_w + al, b_w + bl);
+                        uint16_t h[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            h[q] = OUT == SP24_BF16 ? f32_to_bf16_rne(v[q]) : f32_to_f16_rne(v[q]);
+                        *reinterpret_cast<uint2*>(stg + bl * (EA * 2) + slot(bl, al >> 3) + 8 * ((al >> 2) & 1)) =
+                            make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                    }
+                }
+                // this wave's LDS writes complete before it reads them back
+                __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
+                __builtin_amdgcn_wave_barrier();
+                uint16_t* const y = reinterpret_cast<uint16_t*>(Y);
+#pragma unroll
+                for (int pass = 0; pass < EB / CPP; ++pass) {
+                    const int bl = pass * CPP + lane / CPR, c = lane % CPR;
+                    const uint4 d = *reinterpret_cast<const uint4*>(stg + bl * (EA * 2) + slot(bl, c));
+                    *reinterpret_cast<uint4*>(y + (int64_t)(b_w + bl) * syb + a_w + 8 * c) = d;
+                }
+                return;
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < kFA; ++i) {
 #pragma unroll
@@ -329,11 +391,7 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
             const int br = b0 + wb * 16 * kFB + j * 16 + r;
             if (br >= RB || ar >= RA)
                 continue;
-            f32x4 v = acc_to_f32<DT>(acc[i][j]);
-            const float fsb = sb ? sb[br] : 1.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                v[q] *= (sa && ar + q < RA ? sa[ar + q] : 1.f) * fsb;
+            const f32x4 v = value(i, j, ar, br);
             const int64_t off = (int64_t)ar * sya + (int64_t)br * syb;
             if (sya == 1 && ar + 3 < RA && (off & 3) == 0) {
                 store_out4<OUT>(Y, off, v);
