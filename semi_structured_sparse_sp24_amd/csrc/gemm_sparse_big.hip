@@ -329,57 +329,91 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
             v[q] *= (sa && ar + q < RA ? sa[ar + q] : 1.f) * fsb;
         return v;
     };
-    if constexpr (OUT != SP24_F32 && kFA >= 2) {
+    if constexpr (OUT != SP24_F32) {
+        // A lane's fragment holds four consecutive rows of A in one column b.
         // When A indexes the output's contiguous dimension (sya == 1: the
-        // transposed store of a weight-compressed GEMM), a lane's fragment
-        // holds four consecutive outputs of one column b, so a store
-        // instruction writes 8-byte pieces of 16 columns.  A whole block of
-        // the wave (EA rows of A x EB of B) is instead staged in the free
-        // stage memory, column b as a run of EA outputs, and written back as
-        // whole 16-byte pieces, CPR lanes per column.  The 16-byte chunks of
-        // a staged column are XOR-permuted by the column, so that the 16
-        // columns one fragment writes fall in 16 different bank groups.  (Blocks
-        // of 16 rows of A gain nothing: their columns are 32-byte pieces anyway.)
+        // transposed store of a weight-compressed GEMM) a store instruction
+        // writes 8-byte pieces of 16 output rows; when B does (syb == 1: an
+        // activation-compressed GEMM), 2-byte elements, one instruction per
+        // row of A.  A whole block of the wave (EA rows of A x EB of B) is
+        // instead staged in the stage memory the K loop no longer needs, one
+        // output row after another, and written back as whole 16-byte pieces,
+        // CPR lanes per row.  The 16-byte chunks of a staged row are
+        // XOR-permuted by the row, so that the rows one fragment writes fall
+        // in different bank groups.  (Blocks 16 wide along the contiguous
+        // dimension gain nothing: their rows are 32-byte pieces anyway.)
         constexpr int EA = 16 * kFA, EB = 16 * kFB;
         constexpr int W_STG = EA * EB * 2;             // staging bytes per wave
         constexpr int IN_B = 3 * kBStage / W_STG;      // waves staged in the B stages; the rest in the A stages
         static_assert(kWaves <= IN_B || (kWaves - IN_B) * W_STG <= 3 * kAStage, "staging fits the stages");
-        constexpr int CPR = EA / 8;                    // 16-byte chunks per staged column
-        constexpr int CPP = 64 / CPR;                  // columns per wave-wide read
-        static_assert(CPR >= 4 && CPR <= 16 && EB % CPP == 0, "staged block shape");
+        constexpr int CPR_A = EA / 8, CPR_B = EB / 8;  // 16-byte chunks per staged row, along A or B
+        constexpr int CPP_A = 64 / (CPR_A > 0 ? CPR_A : 1), CPP_B = 64 / (CPR_B > 0 ? CPR_B : 1);   // rows per read
         const int a_w = a0 + wa * EA, b_w = b0 + wb * EB;
-        const bool stage_ok = sya == 1 && (syb & 7) == 0 && ((uintptr_t)Y & 15) == 0;
-        if (stage_ok) {
+        const bool along_a = kFA >= 2 && sya == 1 && (syb & 7) == 0;
+        const bool along_b = kFB >= 2 && syb == 1 && (sya & 7) == 0;
+        if ((along_a || along_b) && ((uintptr_t)Y & 15) == 0) {
             // every wave is done with the stages (its loads past the end have landed)
             __syncthreads();
             if (a_w + EA <= RA && b_w + EB <= RB) {
                 uint8_t* stg = wave < IN_B ? bsb + wave * W_STG : asb + (wave - IN_B) * W_STG;
-                auto slot = [](int bl, int c) { return 16 * (c ^ ((bl / (16 / CPR)) & (CPR - 1))); };
+                uint16_t* const y = reinterpret_cast<uint16_t*>(Y);
+                auto half16 = [](float f) { return OUT == SP24_BF16 ? f32_to_bf16_rne(f) : f32_to_f16_rne(f); };
+                if constexpr (kFA >= 2) {
+                    if (along_a) {
+                        static_assert(CPR_A >= 4 && CPR_A <= 16 && EB % CPP_A == 0, "staged block shape");
+                        // staged row bl (an output row): EA outputs, chunk c at slot c ^ sw(bl)
+                        auto slot = [](int bl, int c) { return 16 * (c ^ ((bl / (16 / CPR_A)) & (CPR_A - 1))); };
 #pragma unroll
-                for (int i = 0; i < kFA; ++i) {
+                        for (int i = 0; i < kFA; ++i) {
 #pragma unroll
-                    for (int j = 0; j < kFB; ++j) {
-                        const int al = i * 16 + 4 * kg, bl = j * 16 + r;
-                        const f32x4 v = value(i, j, a_w + al, b_w + bl);
-                        uint16_t h[4];
+                            for (int j = 0; j < kFB; ++j) {
+                                const int al = i * 16 + 4 * kg, bl = j * 16 + r;
+                                const f32x4 v = value(i, j, a_w + al, b_w + bl);
+                                *reinterpret_cast<uint2*>(stg + bl * (EA * 2) + slot(bl, al >> 3) + 8 * ((al >> 2) & 1)) =
+                                    make_uint2(half16(v[0]) | ((uint32_t)half16(v[1]) << 16),
+                                               half16(v[2]) | ((uint32_t)half16(v[3]) << 16));
+                            }
+                        }
+                        // this wave's LDS writes complete before it reads them back
+                        __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
+                        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            h[q] = OUT == SP24_BF16 ? f32_to_bf16_rne(v[q]) : f32_to_f16_rne(v[q]);
-                        *reinterpret_cast<uint2*>(stg + bl * (EA * 2) + slot(bl, al >> 3) + 8 * ((al >> 2) & 1)) =
-                            make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                        for (int pass = 0; pass < EB / CPP_A; ++pass) {
+                            const int bl = pass * CPP_A + lane / CPR_A, c = lane % CPR_A;
+                            const uint4 d = *reinterpret_cast<const uint4*>(stg + bl * (EA * 2) + slot(bl, c));
+                            *reinterpret_cast<uint4*>(y + (int64_t)(b_w + bl) * syb + a_w + 8 * c) = d;
+                        }
+                        return;
                     }
                 }
-                // this wave's LDS writes complete before it reads them back
-                __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
-                __builtin_amdgcn_wave_barrier();
-                uint16_t* const y = reinterpret_cast<uint16_t*>(Y);
+                if constexpr (kFB >= 2) {
+                    if (along_b) {
+                        static_assert(CPR_B >= 4 && CPR_B <= 16 && EA % CPP_B == 0, "staged block shape");
+                        // staged row al (an output row): EB outputs, chunk c at slot c ^ sw(al)
+                        auto slot = [](int al, int c) { return 16 * (c ^ ((al / (16 / CPR_B)) & (CPR_B - 1))); };
 #pragma unroll
-                for (int pass = 0; pass < EB / CPP; ++pass) {
-                    const int bl = pass * CPP + lane / CPR, c = lane % CPR;
-                    const uint4 d = *reinterpret_cast<const uint4*>(stg + bl * (EA * 2) + slot(bl, c));
-                    *reinterpret_cast<uint4*>(y + (int64_t)(b_w + bl) * syb + a_w + 8 * c) = d;
+                        for (int i = 0; i < kFA; ++i) {
+#pragma unroll
+                            for (int j = 0; j < kFB; ++j) {
+                                const int al = i * 16 + 4 * kg, bl = j * 16 + r;
+                                const f32x4 v = value(i, j, a_w + al, b_w + bl);
+#pragma unroll
+                                for (int q = 0; q < 4; ++q)
+                                    *reinterpret_cast<uint16_t*>(stg + (al + q) * (EB * 2) + slot(al + q, bl >> 3) +
+                                                                 2 * (bl & 7)) = half16(v[q]);
+                            }
+                        }
+                        __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
+                        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                        for (int pass = 0; pass < EA / CPP_B; ++pass) {
+                            const int al = pass * CPP_B + lane / CPR_B, c = lane % CPR_B;
+                            const uint4 d = *reinterpret_cast<const uint4*>(stg + al * (EB * 2) + slot(al, c));
+                            *reinterpret_cast<uint4*>(y + (int64_t)(a_w + al) * sya + b_w + 8 * c) = d;
+                        }
+                        return;
+                    }
                 }
-                return;
             }
         }
     }
