@@ -221,7 +221,8 @@ __device__ __forceinline__ void dense_tile(uint8_t* a0s, uint8_t* a1s, uint8_t* 
         // rows.  As in the sparse tile kernels, a whole block of the wave (EA
         // rows of W x EB rows of X) is staged in the free stage memory, row m
         // of Y as a run of EA outputs with its 16-byte chunks XOR-permuted by
-        // m, and written back as whole 16-byte pieces, CPR lanes per row.
+        // m, and written back as whole 16-byte pieces, CPR lanes per row, by
+        // streaming (non-temporal) stores.
         constexpr int EA = 32 * kFA, EB = 32 * kFB;
         constexpr int W_STG = EA * EB * 2;                    // staging bytes per wave
         constexpr int PA = kBA * 128 / W_STG, PB = kBB * 128 / W_STG;   // waves per W / X stage
@@ -268,7 +269,7 @@ __device__ __forceinline__ void dense_tile(uint8_t* a0s, uint8_t* a1s, uint8_t* 
                 for (int pass = 0; pass < EB / CPP; ++pass) {
                     const int ml = pass * CPP + lane / CPR, c = lane % CPR;
                     const uint4 d = *reinterpret_cast<const uint4*>(stg + ml * (EA * 2) + slot(ml, c));
-                    *reinterpret_cast<uint4*>(y + (int64_t)(m_w + ml) * N + n_w + 8 * c) = d;
+                    store_stream(y + (int64_t)(m_w + ml) * N + n_w + 8 * c, d);
                 }
                 return;
             }

@@ -341,7 +341,9 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
         // CPR lanes per row.  The 16-byte chunks of a staged row are
         // XOR-permuted by the row, so that the rows one fragment writes fall
         // in different bank groups.  (Blocks 16 wide along the contiguous
-        // dimension gain nothing: their rows are 32-byte pieces anyway.)
+        // dimension gain nothing: their rows are 32-byte pieces anyway.)  The
+        // write-back is a streaming (non-temporal) store: the kernel never
+        // reads the output, and the operand panels keep the cache.
         constexpr int EA = 16 * kFA, EB = 16 * kFB;
         constexpr int W_STG = EA * EB * 2;             // staging bytes per wave
         constexpr int IN_B = 3 * kBStage / W_STG;      // waves staged in the B stages; the rest in the A stages
@@ -381,7 +383,7 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
                         for (int pass = 0; pass < EB / CPP_A; ++pass) {
                             const int bl = pass * CPP_A + lane / CPR_A, c = lane % CPR_A;
                             const uint4 d = *reinterpret_cast<const uint4*>(stg + bl * (EA * 2) + slot(bl, c));
-                            *reinterpret_cast<uint4*>(y + (int64_t)(b_w + bl) * syb + a_w + 8 * c) = d;
+                            store_stream(y + (int64_t)(b_w + bl) * syb + a_w + 8 * c, d);
                         }
                         return;
                     }
@@ -409,7 +411,7 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
                         for (int pass = 0; pass < EA / CPP_B; ++pass) {
                             const int al = pass * CPP_B + lane / CPR_B, c = lane % CPR_B;
                             const uint4 d = *reinterpret_cast<const uint4*>(stg + al * (EB * 2) + slot(al, c));
-                            *reinterpret_cast<uint4*>(y + (int64_t)(a_w + al) * sya + b_w + 8 * c) = d;
+                            store_stream(y + (int64_t)(a_w + al) * sya + b_w + 8 * c, d);
                         }
                         return;
                     }

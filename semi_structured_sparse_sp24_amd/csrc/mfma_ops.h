@@ -169,6 +169,11 @@ __device__ __forceinline__ void store_out(void* Y, int64_t off, float v) {
         reinterpret_cast<uint16_t*>(Y)[off] = f32_to_f16_rne(v);
 }
 
+// 16 bytes written with the non-temporal hint (output the kernel never reads back).
+__device__ __forceinline__ void store_stream(void* p, uint4 d) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, d), reinterpret_cast<u32x4*>(p));
+}
+
 // Four consecutive outputs (offset off .. off+3), vectorized when aligned.
 template <sp24_dtype OUT>
 __device__ __forceinline__ void store_out4(void* Y, int64_t off, f32x4 v) {
