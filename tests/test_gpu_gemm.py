@@ -234,6 +234,41 @@ def test_large_tile_kernels_ragged(dt, which, steps, MN):
     assert np.array_equal(decode_out(Y[torch.from_numpy(rows).cuda()]), R)
 
 
+@pytest.mark.parametrize("dt,out", [(oracle.BF16, oracle.BF16), (oracle.F16, oracle.F16), (oracle.BF16, oracle.F16)])
+@pytest.mark.parametrize("which", ["sparse_w", "sparse_x", "dense"])
+@pytest.mark.parametrize("MN", [(4096, 3072), (3900, 3016), (3000, 4100)])
+def test_staged_epilogue_16bit_exact(dt, out, which, MN):
+    """16-bit outputs of the tile kernels, whose epilogue stages whole wave
+    blocks in LDS and writes 16-byte pieces of output rows (along either
+    operand's dimension), with direct stores for blocks cut by the edge and
+    for row strides that are not a multiple of 8 (N = 4100).  Integer
+    inputs keep every sum exact in fp32, so each output must be the RNE
+    encoding of the oracle's value, bit for bit."""
+    M, N = MN
+    K = 256
+    say("staged epilogue", which, dt, out, M, N, K)
+    xb, _, wb, _ = _operands(dt, M, N, K, 321, integer=True)
+    rows = np.array([0, 1, 15, 16, 255, 256, 257, M // 2 + 3, M - 2, M - 1])
+    X, W = to_dev(xb, dt), to_dev(wb, dt)
+    if which == "sparse_w":
+        wv, wm = oracle.prune_compress(dt, wb)
+        R = oracle.gemm(dt, M, N, K, x=xb, w_vals=wv, w_meta=wm, mrows=rows)
+        v, m = sp.prune_compress(W)
+        Y = sp.sp24_gemm(sp.SPARSE_W, v, m, X, M, N, K, out_dtype=OUT_T[out])
+    elif which == "sparse_x":
+        xv, xm = oracle.prune_compress(dt, xb)
+        R = oracle.gemm(dt, M, N, K, x_vals=xv, x_meta=xm, w=wb, mrows=rows)
+        v, m = sp.prune_compress(X)
+        Y = sp.sp24_gemm(sp.SPARSE_X, v, m, W, M, N, K, out_dtype=OUT_T[out])
+    else:
+        wb = oracle.prune(dt, wb)
+        R = oracle.gemm(dt, M, N, K, x=xb, w=wb, mrows=rows)
+        Y = sp.dense_gemm(X, to_dev(wb, dt), out_dtype=OUT_T[out])
+    torch.cuda.synchronize()
+    got = Y[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, oracle.encode(out, R))
+
+
 # 256x256 grids with a short last round, whose remainder runs as quarter
 # tiles: (M, N, K steps) with ragged last tiles in both dimensions
 TAIL = [(4066, 4302, 6), (4096, 5120 - 40, 7), (1000, 68 * 256 - 7, 5)]
