@@ -38,8 +38,8 @@
  *   - fp8 is OCP E4M3 (e4m3fn).  A GEMM takes an optional fp32 scale per row
  *     of X (per token) and per row of W (per output channel), NULL meaning 1:
  *     Y[m][n] = (sum_k x[m][k] * w[n][k]) * scale_x[m] * scale_w[n]
- *     ("FP8 (E4M3) needs only one scale per row or channel": the paper's
- *     section 2, "Quantization").
+ *     (one fp32 scale per row of X and per output channel of W, as the
+ *     2:4-versus-quantization paper's section 2 "Quantization" sets fp8 up).
  *   - Accumulation is fp32; the output is rounded once, to nearest even.
  *   - Every pointer argument is a device pointer unless marked "host".  The
  *     caller allocates and owns every buffer; the library keeps no device

@@ -75,6 +75,8 @@ def _load(path=None):
     lib.oracle_audit.argtypes = [i64, vp, vp, vp, vp, vp, vp, ctypes.c_double, vp, vp]
     lib.oracle_num_threads.restype = i32
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [i32]
     _lib = lib
     return lib
 
@@ -108,6 +110,11 @@ def _ptr(a):
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Worker threads of later oracle calls (for timing the CPU baseline)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def decode(dt: int, bits: np.ndarray) -> np.ndarray:

@@ -510,3 +510,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the number of worker threads of later calls (n >= 1), so that the CPU
+ * baseline can be timed on all threads and on one. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}

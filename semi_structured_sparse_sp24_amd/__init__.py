@@ -131,19 +131,85 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+# ---------------------------------------------------------------- argument checks
+# The kernels size their buffer descriptors and grids from M, N and K alone, so
+# every tensor is checked against them here, before anything reaches the
+# library: shape, row stride, contiguity of K, dtype, and one common device.
+# Shape, stride and dtype mismatches raise ValueError / TypeError; a tensor
+# not on a GPU, or on another GPU than the rest, raises ValueError.
+
+def _mat(t, name, rows, cols, dtype=None, ld_min=None):
+    """t is a rows x cols matrix with contiguous columns.  Its row stride must
+    equal cols, or (ld_min given) be at least ld_min."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dim() != 2 or tuple(t.shape) != (int(rows), int(cols)):
+        raise ValueError(f"{name} must have shape ({rows}, {cols}), got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if rows > 0 and cols > 0:
+        if cols > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must be contiguous along its last axis (stride(1) == 1)")
+        if rows > 1:
+            if ld_min is None and t.stride(0) != cols:
+                raise ValueError(f"{name} must be row-major contiguous (stride(0) == {cols}), "
+                                 f"got stride {t.stride()}")
+            if ld_min is not None and t.stride(0) < ld_min:
+                raise ValueError(f"{name} row stride {t.stride(0)} is below {ld_min}")
+    return t
+
+
+def _vec(t, name, n):
+    """An optional fp32 vector of n contiguous elements (None passes)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor or None")
+    if t.dim() != 1 or t.shape[0] != int(n):
+        raise ValueError(f"{name} must have shape ({n},), got {tuple(t.shape)}")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be torch.float32, got {t.dtype}")
+    if n > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _same_device(*ts):
+    """Every tensor given (None skipped) sits on one GPU; returns that device."""
+    ts = [t for t in ts if t is not None]
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError(f"every operand must be on a GPU, found one on {t.device}")
+        if t.device != dev:
+            raise ValueError(f"operands on different devices: {dev} and {t.device}")
+    return dev
+
+
+def _compressed(values, meta, rows, K, dtype, what):
+    """(values, meta) of a rows x K operand in the library's compressed form."""
+    _mat(values, f"{what} values", rows, K // 2, dtype)
+    _mat(meta, f"{what} meta", rows, (K + 31) // 32, torch.int32)
+
+
 def meta_words_per_row(K: int) -> int:
     return int(lib().sp24_meta_words_per_row(K))
 
 
 def prune_compress(dense: torch.Tensor, values=None, meta=None):
     """Magnitude 2:4 along the last axis: (values rows x K/2, meta rows x ceil(K/32) int32)."""
-    assert dense.dim() == 2 and dense.is_cuda and dense.stride(1) == 1
+    if not isinstance(dense, torch.Tensor) or dense.dim() != 2:
+        raise ValueError("prune_compress takes a 2-D tensor")
     rows, K = dense.shape
+    _mat(dense, "dense", rows, K, ld_min=K)
     if values is None:
         values = torch.empty((rows, K // 2), dtype=dense.dtype, device=dense.device)
     if meta is None:
         meta = torch.empty((rows, (K + 31) // 32), dtype=torch.int32, device=dense.device)
-    st = lib().sp24_prune_compress(_code(dense), rows, K, _ptr(dense), dense.stride(0), _ptr(values),
+    _compressed(values, meta, rows, K, dense.dtype, "output")
+    _same_device(dense, values, meta)
+    ld = dense.stride(0) if rows > 1 else K
+    st = lib().sp24_prune_compress(_code(dense), rows, K, _ptr(dense), ld, _ptr(values),
                                    _ptr(meta), _stream(dense.device))
     _check("sp24_prune_compress", st)
     return values, meta
@@ -152,15 +218,21 @@ def prune_compress(dense: torch.Tensor, values=None, meta=None):
 def quantize_prune_compress(x: torch.Tensor, values=None, meta=None, scales=None):
     """Per-row e4m3 quantization fused with the 2:4 prune and compress:
     (values rows x K/2 e4m3, meta rows x K/32 int32, scales rows fp32)."""
-    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("quantize_prune_compress takes a 2-D tensor")
     rows, K = x.shape
+    _mat(x, "x", rows, K, ld_min=K)
     if values is None:
         values = torch.empty((rows, K // 2), dtype=torch.float8_e4m3fn, device=x.device)
     if meta is None:
         meta = torch.empty((rows, (K + 31) // 32), dtype=torch.int32, device=x.device)
     if scales is None:
         scales = torch.empty(rows, dtype=torch.float32, device=x.device)
-    st = lib().sp24_quantize_prune_compress(_code(x), rows, K, _ptr(x), x.stride(0), _ptr(values), _ptr(meta),
+    _compressed(values, meta, rows, K, torch.float8_e4m3fn, "output")
+    _vec(scales, "scales", rows)
+    _same_device(x, values, meta, scales)
+    ld = x.stride(0) if rows > 1 else K
+    st = lib().sp24_quantize_prune_compress(_code(x), rows, K, _ptr(x), ld, _ptr(values), _ptr(meta),
                                             _ptr(scales), _stream(x.device))
     _check("sp24_quantize_prune_compress", st)
     return values, meta, scales
@@ -168,33 +240,61 @@ def quantize_prune_compress(x: torch.Tensor, values=None, meta=None, scales=None
 
 def quantize_e4m3(x: torch.Tensor, out=None, scales=None):
     """Per-row e4m3 quantization: (codes rows x K e4m3, scales rows fp32)."""
-    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("quantize_e4m3 takes a 2-D tensor")
     rows, K = x.shape
+    _mat(x, "x", rows, K, ld_min=K)
     if out is None:
         out = torch.empty((rows, K), dtype=torch.float8_e4m3fn, device=x.device)
     if scales is None:
         scales = torch.empty(rows, dtype=torch.float32, device=x.device)
-    st = lib().sp24_quantize_e4m3(_code(x), rows, K, _ptr(x), x.stride(0), _ptr(out), _ptr(scales),
+    _mat(out, "out", rows, K, torch.float8_e4m3fn)
+    _vec(scales, "scales", rows)
+    _same_device(x, out, scales)
+    ld = x.stride(0) if rows > 1 else K
+    st = lib().sp24_quantize_e4m3(_code(x), rows, K, _ptr(x), ld, _ptr(out), _ptr(scales),
                                   _stream(x.device))
     _check("sp24_quantize_e4m3", st)
     return out, scales
 
 
 def decompress(values: torch.Tensor, meta: torch.Tensor, K: int, out=None):
+    """The dense rows x K operand: kept values in place, +0 elsewhere."""
+    if not isinstance(values, torch.Tensor) or values.dim() != 2:
+        raise ValueError("decompress takes 2-D values")
     rows = values.shape[0]
+    _compressed(values, meta, rows, K, values.dtype, "input")
     if out is None:
         out = torch.empty((rows, K), dtype=values.dtype, device=values.device)
-    st = lib().sp24_decompress(_code(values), rows, K, _ptr(values), _ptr(meta), _ptr(out), out.stride(0),
+    _mat(out, "out", rows, K, values.dtype, ld_min=K)
+    _same_device(values, meta, out)
+    ld = out.stride(0) if rows > 1 else K
+    st = lib().sp24_decompress(_code(values), rows, K, _ptr(values), _ptr(meta), _ptr(out), ld,
                                _stream(values.device))
     _check("sp24_decompress", st)
     return out
 
 
+def _out(out, M, N, out_dtype, device):
+    if out is None:
+        return torch.empty((M, N), dtype=out_dtype, device=device)
+    return _mat(out, "out", M, N)
+
+
 def sp24_gemm(which: int, values, meta, dense, M: int, N: int, K: int, out_dtype=torch.bfloat16,
               scale_x=None, scale_w=None, out=None):
     """Y (M x N) = X W^T with W (which=SPARSE_W) or X (which=SPARSE_X) given as (values, meta)."""
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=dense.device)
+    if which not in (SPARSE_W, SPARSE_X):
+        raise ValueError(f"which must be SPARSE_W or SPARSE_X, got {which}")
+    if not isinstance(dense, torch.Tensor):
+        raise TypeError("dense must be a torch.Tensor")
+    rows, other = (N, M) if which == SPARSE_W else (M, N)
+    _mat(dense, "dense", other, K)
+    _compressed(values, meta, rows, K, dense.dtype, "compressed operand")
+    _vec(scale_x, "scale_x", M)
+    _vec(scale_w, "scale_w", N)
+    out = _out(out, M, N, out_dtype, dense.device)
+    _same_device(dense, values, meta, scale_x, scale_w, out)
     st = lib().sp24_gemm(which, _code(dense), _code(out), M, N, K, _ptr(values), _ptr(meta), _ptr(dense),
                          _ptr(scale_x), _ptr(scale_w), _ptr(out), _stream(dense.device))
     _check("sp24_gemm", st)
@@ -202,10 +302,17 @@ def sp24_gemm(which: int, values, meta, dense, M: int, N: int, K: int, out_dtype
 
 
 def dense_gemm(x, w, out_dtype=torch.bfloat16, scale_x=None, scale_w=None, out=None):
+    """Y (M x N) = X W^T on dense operands, the baseline and the fallback."""
+    if not isinstance(x, torch.Tensor) or not isinstance(w, torch.Tensor) or x.dim() != 2 or w.dim() != 2:
+        raise ValueError("dense_gemm takes 2-D tensors")
     M, K = x.shape
     N = w.shape[0]
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _mat(x, "x", M, K)
+    _mat(w, "w", N, K, x.dtype)
+    _vec(scale_x, "scale_x", M)
+    _vec(scale_w, "scale_w", N)
+    out = _out(out, M, N, out_dtype, x.device)
+    _same_device(x, w, scale_x, scale_w, out)
     st = lib().dense_gemm(_code(x), _code(out), M, N, K, _ptr(x), _ptr(w), _ptr(scale_x), _ptr(scale_w),
                           _ptr(out), _stream(x.device))
     _check("dense_gemm", st)
@@ -216,9 +323,18 @@ def hybrid_gemm(values, meta, w_dense, x, N_s: int, N_d: int, out_dtype=torch.bf
                 scale_w=None, out=None):
     """Y (M x (N_s + N_d)): columns [0, N_s) from the compressed rows (values, meta), the rest from the
     dense rows w_dense (N_d x K); one launch.  values / meta / w_dense may be None for an empty region."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("hybrid_gemm takes a 2-D x")
     M, K = x.shape
-    if out is None:
-        out = torch.empty((M, N_s + N_d), dtype=out_dtype, device=x.device)
+    _mat(x, "x", M, K)
+    if N_s > 0 or values is not None or meta is not None:
+        _compressed(values, meta, N_s, K, x.dtype, "sparse rows")
+    if N_d > 0 or w_dense is not None:
+        _mat(w_dense, "w_dense", N_d, K, x.dtype)
+    _vec(scale_x, "scale_x", M)
+    _vec(scale_w, "scale_w", N_s + N_d)
+    out = _out(out, M, N_s + N_d, out_dtype, x.device)
+    _same_device(x, values, meta, w_dense, scale_x, scale_w, out)
     st = lib().sp24_hybrid_gemm(_code(x), _code(out), M, N_s, N_d, K, _ptr(values), _ptr(meta), _ptr(w_dense),
                                 _ptr(x), _ptr(scale_x), _ptr(scale_w), _ptr(out), _stream(x.device))
     _check("sp24_hybrid_gemm", st)
@@ -234,9 +350,19 @@ def hybrid_kernel(in_dtype, out_dtype, M: int, N_s: int, N_d: int, K: int):
 def select_tactic(which, values, meta, dense_other, dense_pruned, M, N, K, out_dtype=torch.bfloat16,
                   scale_x=None, scale_w=None, y_scratch=None, warmup=5, reps=20):
     """Times sparse(+compress) against dense on these buffers; returns the tactic record."""
+    if which not in (SPARSE_W, SPARSE_X):
+        raise ValueError(f"which must be SPARSE_W or SPARSE_X, got {which}")
+    if not isinstance(dense_other, torch.Tensor):
+        raise TypeError("dense_other must be a torch.Tensor")
+    rows, other = (N, M) if which == SPARSE_W else (M, N)
+    _mat(dense_other, "dense_other", other, K)
+    _mat(dense_pruned, "dense_pruned", rows, K, dense_other.dtype)
+    _compressed(values, meta, rows, K, dense_other.dtype, "compressed operand")
+    _vec(scale_x, "scale_x", M)
+    _vec(scale_w, "scale_w", N)
     dev = dense_other.device
-    if y_scratch is None:
-        y_scratch = torch.empty((M, N), dtype=out_dtype, device=dev)
+    y_scratch = _out(y_scratch, M, N, out_dtype, dev)
+    _same_device(dense_other, dense_pruned, values, meta, scale_x, scale_w, y_scratch)
     rec = Tactic()
     st = lib().sp24_select_tactic(which, _code(dense_other), _code(y_scratch), M, N, K, _ptr(values),
                                   _ptr(meta), _ptr(dense_other), _ptr(dense_pruned), _ptr(scale_x),

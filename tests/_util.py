@@ -38,9 +38,26 @@ def to_host(t: torch.Tensor, dt: int) -> np.ndarray:
     return t.detach().contiguous().cpu().view(VIEW_OF[dt]).numpy().view(NP_OF[dt])
 
 
+def meta_dev(m: np.ndarray) -> torch.Tensor:
+    """Metadata words (uint32) as the int32 device tensor the binding takes."""
+    return torch.from_numpy(np.ascontiguousarray(m, dtype=np.uint32).view(np.int32)).cuda()
+
+
 def meta_host(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().numpy().view(np.uint32)
 
 
 def decode_out(Y: torch.Tensor) -> np.ndarray:
     return Y.detach().float().cpu().numpy().astype(np.float64)
+
+
+def band_rows(M: int, band: int = 256, seed: int = 0) -> np.ndarray:
+    """Rows of M to compare at full size: all of them up to 64 rows; beyond,
+    one row at a seeded place in every band of 256 rows (one per band of
+    output tiles), plus rows 0 and M - 1."""
+    if M <= 64:
+        return np.arange(M, dtype=np.int64)
+    rng = np.random.default_rng(seed + M)
+    starts = np.arange(0, M, band)
+    picks = starts + rng.integers(0, band, size=len(starts))
+    return np.unique(np.clip(np.r_[0, picks, M - 1], 0, M - 1)).astype(np.int64)

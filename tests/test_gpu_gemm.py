@@ -9,6 +9,8 @@ dense GEMM against the oracle's fp64 product on the decompressed operand:
     checked on sampled rows of M;
   - edge cases: empty outputs, K = 0, ineligible K, guard bands, reruns.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -16,7 +18,7 @@ import torch
 import oracle
 import semi_structured_sparse_sp24_amd as sp
 from semi_structured_sparse_sp24_amd import inputs
-from tests._util import TOL, decode_out, say, to_dev, to_host
+from tests._util import TOL, band_rows, decode_out, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -337,8 +339,19 @@ def test_one_hot_rows_read_back_weights():
 # ------------------------------------------------------------------ full size
 
 def _sample_rows(M):
-    rows = sorted({0, M - 1, M // 2, (M * 7) // 11})
-    return np.array([r for r in rows if 0 <= r < M], dtype=np.int64)
+    """One row from every 256-row band of M (a seeded place in the band, so
+    that every band of tiles is checked), plus the first and the last row."""
+    return band_rows(M)
+
+
+@functools.lru_cache(maxsize=1)
+def _full_weight(wl, s):
+    """A workload's weight (bits, scales) and the oracle's compressed form of
+    it, kept for the next M of the same shape."""
+    dt = inputs.WORKLOADS[wl]["dtype"]
+    wb, sw = inputs.weight(wl, s)
+    wv, wm = oracle.prune_compress(dt, wb)
+    return wb, sw, wv, wm
 
 
 FULL = []
@@ -356,9 +369,8 @@ def test_full_size_sparse_and_dense(wl, s, j):
     N, K = w["shapes"][s]
     M = w["ms"][j]
     say("full", wl, (N, K), "M", M)
-    wb, sw = inputs.weight(wl, s)
+    wb, sw, wv, wm = _full_weight(wl, s)
     xb, sx = inputs.activation(wl, s, j)
-    wv, wm = oracle.prune_compress(dt, wb)
     rows = np.arange(M) if M <= 16 else _sample_rows(M)
     R = oracle.gemm(dt, M, N, K, x=xb, w_vals=wv, w_meta=wm, scale_x=sx, scale_w=sw, mrows=rows)
     W = to_dev(wb, dt)

@@ -11,7 +11,7 @@ import torch
 import oracle
 import semi_structured_sparse_sp24_amd as sp
 from semi_structured_sparse_sp24_amd import inputs
-from tests._util import TOL, decode_out, say, to_dev
+from tests._util import TOL, decode_out, meta_dev, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ def _run(dt, out_dt, M, NS, ND, K, seed, sample=None, integer=False):
     say("hybrid", dt, out_dt, M, NS, ND, K, name)
     dev = lambda a, d: None if a is None or a.size == 0 else to_dev(a, d)
     tf = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
-    Y = sp.hybrid_gemm(dev(v, dt), dev(m, oracle.F32) if NS else None, dev(wd, dt), dev(x, dt), NS, ND,
+    Y = sp.hybrid_gemm(dev(v, dt), meta_dev(m) if NS else None, dev(wd, dt), dev(x, dt), NS, ND,
                        out_dtype=OUT[out_dt], scale_x=tf(sx), scale_w=tf(sw))
     torch.cuda.synchronize()
     rows = np.arange(M) if sample is None else np.unique(np.r_[0, M - 1, np.random.default_rng(seed).integers(0, M, sample)])
@@ -84,7 +84,7 @@ def test_hybrid_tail_quarter_tiles(M, NS, ND):
     x, wd, v, m, sx, sw = _operands(oracle.BF16, M, NS, ND, K, 11 + M, integer=True)
     say("hybrid tail", M, NS, ND, K)
     Y = torch.full((M, NS + ND), float("nan"), dtype=torch.float32, device="cuda")
-    sp.hybrid_gemm(to_dev(v, oracle.BF16), to_dev(m, oracle.F32), to_dev(wd, oracle.BF16), to_dev(x, oracle.BF16),
+    sp.hybrid_gemm(to_dev(v, oracle.BF16), meta_dev(m), to_dev(wd, oracle.BF16), to_dev(x, oracle.BF16),
                    NS, ND, out=Y)
     torch.cuda.synchronize()
     assert torch.isfinite(Y).all()
@@ -113,7 +113,7 @@ def test_hybrid_dense_region_equals_the_plain_gemms():
     (within the bar: the dense block adds in another order)."""
     dt, M, NS, ND, K = oracle.BF16, 512, 1024, 512, 1024
     x, wd, v, m, _, _ = _operands(dt, M, NS, ND, K, 11)
-    X, V, Mt, Wd = to_dev(x, dt), to_dev(v, dt), to_dev(m, oracle.F32), to_dev(wd, dt)
+    X, V, Mt, Wd = to_dev(x, dt), to_dev(v, dt), meta_dev(m), to_dev(wd, dt)
     Y = sp.hybrid_gemm(V, Mt, Wd, X, NS, ND)
     Ys = sp.sp24_gemm(sp.SPARSE_W, V, Mt, X, M, NS, K)
     Yd = sp.dense_gemm(X, Wd)
