@@ -256,6 +256,24 @@ def hybrid_gemm(dt: int, M: int, NS: int, ND: int, K: int, *, x, ws_vals=None, w
     return R
 
 
+def ksplit_gemm(dt: int, M: int, N: int, KS: int, K: int, *, x, ws_vals, ws_meta, wd, scale_x=None,
+                scale_w=None, mrows=None):
+    """The K-split hybrid ("Production 2:4 Structured Sparsity for LLMs",
+    "Dense Fallback and Hybrid Sparsity Design"; the SlideSparse page's
+    Spense abstract: each weight split into a 2:4 region and a dense region):
+    columns [0, KS) of every weight row are 2:4 (given compressed), columns
+    [KS, K) dense (wd, N x (K - KS)).  The weight is the two ranges side by
+    side along K, the 2:4 range decompressed; R = X W^T over that weight, the
+    plain product of gemm()."""
+    KD = K - KS
+    assert 0 <= KS <= K
+    ws = decompress(dt, ws_vals, ws_meta, KS) if KS > 0 else np.zeros((N, 0), dtype=_bits_dtype(dt))
+    wd = np.zeros((N, 0), dtype=_bits_dtype(dt)) if KD == 0 else np.ascontiguousarray(wd, dtype=_bits_dtype(dt))
+    assert ws.shape == (N, KS) and wd.shape == (N, KD)
+    w = np.ascontiguousarray(np.concatenate([ws, wd], axis=1))
+    return gemm(dt, M, N, K, x=x, w=w, scale_x=scale_x, scale_w=scale_w, mrows=mrows)
+
+
 def audit_metrics(records, counts, other_time_us: float = 0.0) -> dict:
     """Manifest metrics over layer records (dicts with eligible, selected
     ("sparse" / "dense"), t_sparse_us, t_compress_us, t_dense_us), record i

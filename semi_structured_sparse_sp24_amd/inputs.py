@@ -23,6 +23,9 @@ Workloads, shaped like the linear layers of the pages' LLMs:
   online_fp8  the same X (bf16, outliers), quantized to e4m3 per row and
             pruned on every call by the library; W e4m3 (N, K) in
             {(4096,4096), (28672,4096)} with per-channel scales; M = 4096
+  int8      the fp8 shapes in symmetric per-row int8
+  hybrid    the prefill weights, the last N/8 rows kept dense; M in {2048, 8192}
+  ksplit    the prefill weights, the last K/4 columns kept dense; M in {2048, 8192}
 Seed of tensor t (0 = W, 1 = X, 2 = outlier mask) of shape s in workload c at
 M index j:  10000*c + 100*s + 10*t + j.
 """
@@ -59,6 +62,9 @@ WORKLOADS = {
     # the prefill layers with one output row in eight kept dense (hybrid_split)
     "hybrid": dict(index=7, dtype=BF16, out=BF16,
                    shapes=[(4096, 4096), (6144, 4096), (28672, 4096), (4096, 14336)], ms=[2048, 8192]),
+    # the prefill layers with the last quarter of K kept dense (ksplit_split)
+    "ksplit": dict(index=9, dtype=BF16, out=BF16,
+                   shapes=[(4096, 4096), (6144, 4096), (28672, 4096), (4096, 14336)], ms=[2048, 8192]),
 }
 
 
@@ -67,6 +73,13 @@ def hybrid_split(N: int) -> tuple[int, int]:
     last N/8 rows (a multiple of 256) stay dense."""
     nd = max(256, N // 8 // 256 * 256)
     return N - nd, nd
+
+
+def ksplit_split(K: int) -> tuple[int, int]:
+    """(2:4 columns, dense columns) of a K-wide weight in the ksplit workload:
+    the last K/4 columns (a multiple of 256) stay dense."""
+    kd = max(256, K // 4 // 256 * 256)
+    return K - kd, kd
 
 
 def seed_of(c: int, s: int, t: int, j: int) -> int:
