@@ -171,22 +171,30 @@ def build_cases(workload, cold):
         wb, sw = inputs.weight(workload, s)
         W0 = dev(wb, dt)
         shape = {"s": s, "N": N, "K": K, "sw": None if sw is None else torch.from_numpy(sw).cuda(), "ms": []}
-        NS = N
+        NS, KS = N, K
         if workload == HYBRID:
             # the first NS rows go 2:4, the rest stay dense; the dense baseline runs the same weight
             # (the pruned rows and the dense rows) through the dense GEMM
             NS, ND = inputs.hybrid_split(N)
             shape.update(NS=NS, ND=ND, Wd=W0[NS:].contiguous())
             W0 = W0[:NS].contiguous()
-        nc = 1 if workload in ONLINE else n_copies(NS * K * eb // 2 + NS * K // 8, cold)
+        if workload == KSPLIT:
+            # the first KS columns of every row go 2:4, the rest stay dense; the dense baseline runs the
+            # same weight (the pruned range and the dense range) through the dense GEMM
+            KS, KD = inputs.ksplit_split(K)
+            shape.update(KS=KS, KD=KD, Wd=W0[:, KS:].contiguous())
+            W0 = W0[:, :KS].contiguous()
+        nc = 1 if workload in ONLINE else n_copies(NS * KS * eb // 2 + NS * KS // 8, cold)
         copies = []
         for i in range(nc):
             W = W0 if i == 0 else W0.clone()
             v, m = sp.prune_compress(W)
-            copies.append({"W": W, "v": v, "m": m, "Wp": sp.decompress(v, m, K)})
+            copies.append({"W": W, "v": v, "m": m, "Wp": sp.decompress(v, m, KS)})
         shape["copies"] = copies
         if workload == HYBRID:
             shape["Wfull"] = torch.cat([copies[0]["Wp"], shape["Wd"]]).contiguous()
+        if workload == KSPLIT:
+            shape["Wfull"] = torch.cat([copies[0]["Wp"], shape["Wd"]], dim=1).contiguous()
         for j, M in enumerate(w["ms"]):
             xb, sx = inputs.activation(workload, s, j)
             X = dev(xb, w.get("act", dt))
@@ -226,10 +234,11 @@ def chains(workload, cases):
         N, K, cp = c["N"], c["K"], c["copies"]
         pick = lambda i, cp=cp: cp[i % len(cp)]
         if workload not in ONLINE:
+            Kc = c.get("KS", K)
             out.append((("compress", c["s"]), Lc,
                         lambda i, pick=pick: sp.prune_compress(pick(i)["W"], values=pick(i)["v"], meta=pick(i)["m"])))
             out.append((("decompress", c["s"]), Lc,
-                        lambda i, pick=pick, K=K: sp.decompress(pick(i)["v"], pick(i)["m"], K, out=pick(i)["Wp"])))
+                        lambda i, pick=pick, Kc=Kc: sp.decompress(pick(i)["v"], pick(i)["m"], Kc, out=pick(i)["Wp"])))
         for it in c["ms"]:
             M, key = it["M"], (c["s"], it["j"])
             if workload == "online_fp8":
@@ -260,6 +269,14 @@ def chains(workload, cases):
                     sp.sp24_gemm(sp.SPARSE_W, pick(i)["v"], pick(i)["m"], it["X"], M, NS, K, out=it["Ys"])
                     sp.dense_gemm(it["X"], Wd, out=it["Ydd"])
                 out.append((("split",) + key, Lg, split))
+                continue
+            if workload == KSPLIT:
+                # one launch for both K ranges, against the dense GEMM on the whole weight
+                KS, Wd, Wf = c["KS"], c["Wd"], c["Wfull"]
+                out.append((("sparse",) + key, Lg,
+                            lambda i, it=it, pick=pick, Wd=Wd, N=N, KS=KS:
+                            sp.ksplit_gemm(pick(i)["v"], pick(i)["m"], Wd, it["X"], N, KS, out=it["Y"])))
+                out.append((("dense",) + key, Lg, lambda i, it=it, Wf=Wf: sp.dense_gemm(it["X"], Wf, out=it["Yd"])))
                 continue
             if workload == "online":
                 # the activation is the sparse operand: prune+compress it on every call
@@ -599,9 +616,7 @@ def measure(workload, args, steps, warmup, cpu_budget, eager=False):
                 row.update(N_s=c["NS"], N_d=c["ND"], t_two_launch_us=round(tsp, 2),
                            speedup_vs_two_launch=round(tsp / tsm, 3))
             if workload == KSPLIT:
-                tsp = float(np.median(times[("split",) + key]))
-                row.update(K_s=c["KS"], K_d=c["KD"], t_two_launch_us=round(tsp, 2),
-                           speedup_vs_two_launch=round(tsp / tsm, 3))
+                row.update(K_s=c["KS"], K_d=c["KD"])
             if workload in ONLINE:
                 tc = float(np.median(times[("compress",) + key]))
                 tp = float(np.median(times[("prep",) + key])) if workload == "online_fp8" else 0.0

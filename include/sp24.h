@@ -236,6 +236,42 @@ const char *sp24_hybrid_kernel(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, i
                                int64_t N_d, int64_t K);
 
 /*
+ * Hybrid sparse + dense GEMM split along K, in one launch ("Production 2:4
+ * Structured Sparsity for LLMs", section "Dense Fallback and Hybrid Sparsity
+ * Design"; the SlideSparse page, Spense abstract: each weight matrix split
+ * into a 2:4 region and a dense region).  Columns [0, K_s) of every weight
+ * row are 2:4-compressed, columns [K_s, K) stay dense, and both ranges add
+ * into the same outputs:
+ *   Y[m][n] = sum_{k < K_s} X[m][k] * Ws[n][k] + sum_{k >= K_s} X[m][k] * Wd[n][k - K_s]
+ * (times scale_x[m] * scale_w[n] for 8-bit inputs), accumulated in one fp32
+ * (int32 for int8) accumulator per output and rounded once.  The caller
+ * chooses which columns go where (a permutation of K applied to the columns
+ * of both W and X leaves Y unchanged).  Each workgroup runs the 2:4 range of
+ * its tile on the sparse instruction and then the dense range on the dense
+ * one, into the same registers.
+ *   in_dt, out_dt  as sp24_gemm
+ *   M, N, K_s, K   M, N >= 0; 0 <= K_s <= K, else SP24_E_SHAPE; K % 64
+ *                  (16-bit) or K % 128 (8-bit), and K_s % 256, else
+ *                  SP24_E_ALIGN
+ *   values, meta   Ws compressed: N x K_s/2 values, N x K_s/32 words
+ *   W_d            N x (K - K_s) dense, row-major (row stride K - K_s)
+ *   X              M x K dense, row-major
+ *   scale_x        M floats or NULL;  scale_w  N floats or NULL
+ *   Y              M x N of out_dt, row-major
+ * Same size limits, alignment and errors as sp24_gemm; values/meta may be
+ * NULL when K_s == 0 and W_d when K_s == K.
+ */
+sp24_status sp24_ksplit_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K_s,
+                             int64_t K, const void *values, const uint32_t *meta, const void *W_d,
+                             const void *X, const float *scale_x, const float *scale_w, void *Y,
+                             hipStream_t stream);
+
+/* The name of the kernel sp24_ksplit_gemm launches for this shape (host
+ * only; NULL if rejected). */
+const char *sp24_ksplit_kernel(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N,
+                               int64_t K_s, int64_t K);
+
+/*
  * The name of the kernel that sp24_gemm (sparse != 0) or dense_gemm
  * (sparse == 0) launches for this shape and dtype, without launching
  * anything: a pure host function, no HIP call.  The same names appear in

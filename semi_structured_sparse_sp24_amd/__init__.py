@@ -16,6 +16,7 @@ PyTorch fallback: if the library is missing, every call raises.
   quantize_prune_compress(x)   -> (values e4m3, meta, scales): fused online fp8 path
   quantize_e4m3(x)             -> (codes e4m3, scales): the dense side's quantization
   hybrid_gemm(...)             -> Y = X [Ws | Wd]^T, Ws compressed and Wd dense rows, one launch
+  ksplit_gemm(...)             -> Y = X W^T, W's first K_s columns compressed and the rest dense, one launch
   audit_aggregate(...)         -> layer counts, ratios and Sparse GPU-Time Coverage (host only)
 """
 from __future__ import annotations
@@ -76,6 +77,8 @@ SIGNATURES = {
     "sp24_gemm_kernel": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i64, _i64, _i64]),
     "sp24_hybrid_gemm": (_i32, [_i32, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "sp24_hybrid_kernel": (ctypes.c_char_p, [_i32, _i32, _i64, _i64, _i64, _i64]),
+    "sp24_ksplit_gemm": (_i32, [_i32, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "sp24_ksplit_kernel": (ctypes.c_char_p, [_i32, _i32, _i64, _i64, _i64, _i64]),
     "sp24_audit_aggregate": (_i32, [ctypes.POINTER(Tactic), ctypes.POINTER(_i64), _i64, _dbl,
                                     ctypes.POINTER(AuditMetrics)]),
     "sp24_quantize_prune_compress": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp]),
@@ -344,6 +347,37 @@ def hybrid_gemm(values, meta, w_dense, x, N_s: int, N_d: int, out_dtype=torch.bf
 def hybrid_kernel(in_dtype, out_dtype, M: int, N_s: int, N_d: int, K: int):
     """Name of the kernel hybrid_gemm launches for this shape; None if rejected."""
     name = lib().sp24_hybrid_kernel(DTYPE_CODE[in_dtype], DTYPE_CODE[out_dtype], M, N_s, N_d, K)
+    return None if name is None else name.decode()
+
+
+def ksplit_gemm(values, meta, w_dense, x, N: int, K_s: int, out_dtype=torch.bfloat16, scale_x=None,
+                scale_w=None, out=None):
+    """Y (M x N) = X W^T with W's columns [0, K_s) given compressed (values N x K_s/2, meta) and
+    columns [K_s, K) dense (w_dense N x (K - K_s)); one launch.  values / meta may be None when
+    K_s == 0, w_dense when K_s == K."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("ksplit_gemm takes a 2-D x")
+    M, K = x.shape
+    if not 0 <= K_s <= K:
+        raise ValueError(f"K_s must lie in [0, {K}], got {K_s}")
+    _mat(x, "x", M, K)
+    if K_s > 0 or values is not None or meta is not None:
+        _compressed(values, meta, N, K_s, x.dtype, "2:4 range")
+    if K_s < K or w_dense is not None:
+        _mat(w_dense, "w_dense", N, K - K_s, x.dtype)
+    _vec(scale_x, "scale_x", M)
+    _vec(scale_w, "scale_w", N)
+    out = _out(out, M, N, out_dtype, x.device)
+    _same_device(x, values, meta, w_dense, scale_x, scale_w, out)
+    st = lib().sp24_ksplit_gemm(_code(x), _code(out), M, N, K_s, K, _ptr(values), _ptr(meta), _ptr(w_dense),
+                                _ptr(x), _ptr(scale_x), _ptr(scale_w), _ptr(out), _stream(x.device))
+    _check("sp24_ksplit_gemm", st)
+    return out
+
+
+def ksplit_kernel(in_dtype, out_dtype, M: int, N: int, K_s: int, K: int):
+    """Name of the kernel ksplit_gemm launches for this shape; None if rejected."""
+    name = lib().sp24_ksplit_kernel(DTYPE_CODE[in_dtype], DTYPE_CODE[out_dtype], M, N, K_s, K)
     return None if name is None else name.decode()
 
 

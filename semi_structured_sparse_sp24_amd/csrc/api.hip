@@ -335,6 +335,85 @@ SP24_API const char* sp24_hybrid_kernel(sp24_dtype in_dt, sp24_dtype out_dt, int
     return name;
 }
 
+// Dtype and size checks of the K-split hybrid GEMM (no pointer is looked at).
+static sp24_status check_ksplit_shape(const sp24_dtype& in_dt, const sp24_dtype& out_dt, int64_t M, int64_t N,
+                                      int64_t K_s, int64_t K) {
+    if (!dtype_known(enum_bits(in_dt)) || !dtype_known(enum_bits(out_dt)) || !is_input_dtype(in_dt) ||
+        !out_ok(in_dt, out_dt))
+        return SP24_E_DTYPE;
+    if (K_s < 0 || K_s > K)
+        return SP24_E_SHAPE;
+    // the whole weight is N x K: the plain GEMM's limits and K tile cover both ranges
+    sp24_status st = check_shape(in_dt, out_dt, M, N, K, true);
+    if (st != SP24_OK)
+        return st;
+    // the compressed range in whole metadata blocks (8 words of a row)
+    if (M > 0 && N > 0 && K_s % 256 != 0)
+        return SP24_E_ALIGN;
+    return SP24_OK;
+}
+
+SP24_API sp24_status sp24_ksplit_gemm(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K_s,
+                                      int64_t K, const void* values, const uint32_t* meta, const void* W_d,
+                                      const void* X, const float* scale_x, const float* scale_w, void* Y,
+                                      hipStream_t stream) {
+    if (!dtype_known(enum_bits(in_dt)) || !dtype_known(enum_bits(out_dt)) || !is_input_dtype(in_dt) ||
+        !out_ok(in_dt, out_dt))
+        return SP24_E_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0 || K_s < 0 || K_s > K)
+        return SP24_E_SHAPE;
+    if (M > 0 && N > 0) {
+        if (!Y)
+            return SP24_E_NULL;
+        if (K > 0 && (!X || (K_s > 0 && (!values || !meta)) || (K_s < K && !W_d)))
+            return SP24_E_NULL;
+    }
+    sp24_status st = check_ksplit_shape(in_dt, out_dt, M, N, K_s, K);
+    if (st != SP24_OK || M == 0 || N == 0)
+        return st;
+    if (!aligned16(Y) || ((uintptr_t)scale_x & 3u) || ((uintptr_t)scale_w & 3u) || !aligned16(X) ||
+        (K_s > 0 && (!aligned16(values) || !aligned16(meta))) || (K_s < K && !aligned16(W_d)))
+        return SP24_E_ALIGN;
+    if (K == 0)
+        return launch_fill_zero(Y, M * N * elem_bytes(out_dt), stream) == hipSuccess ? SP24_OK : SP24_E_HIP;
+    KsplitArgs k;
+    k.in_dt = in_dt;
+    k.out_dt = out_dt;
+    k.M = M;
+    k.N = N;
+    k.KS = K_s;
+    k.K = K;
+    k.ws_vals = values;
+    k.ws_meta = meta;
+    k.wd = W_d;
+    k.x = X;
+    k.scale_x = scale_x;
+    k.scale_w = scale_w;
+    k.Y = Y;
+    return launch_sp24_ksplit(k, stream, nullptr) == hipSuccess ? SP24_OK : SP24_E_HIP;
+}
+
+SP24_API const char* sp24_ksplit_kernel(sp24_dtype in_dt, sp24_dtype out_dt, int64_t M, int64_t N, int64_t K_s,
+                                       int64_t K) {
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0 || check_ksplit_shape(in_dt, out_dt, M, N, K_s, K) != SP24_OK)
+        return nullptr;
+    if (M == 0 || N == 0)
+        return "none";
+    if (K == 0)
+        return "fill_zero";
+    KsplitArgs k{};
+    k.in_dt = in_dt;
+    k.out_dt = out_dt;
+    k.M = M;
+    k.N = N;
+    k.KS = K_s;
+    k.K = K;
+    k.dry = true;
+    const char* name = nullptr;
+    launch_sp24_ksplit(k, nullptr, &name);
+    return name;
+}
+
 SP24_API const char* sp24_gemm_kernel(int sparse, sp24_operand which, sp24_dtype in_dt, sp24_dtype out_dt,
                                      int64_t M, int64_t N, int64_t K) {
     const int w = enum_bits(which);

@@ -96,6 +96,48 @@ __device__ __forceinline__ void split_halves(const uint4& q0, const uint4& q1, u
     }
 }
 
+// The dense K range of a K-split weight: one 16x16 dense MFMA per fragment
+// and half step, a half step being 64 bytes of a row (32 16-bit or 64 8-bit
+// elements).  A lane supplies the 16 bytes at 16 * kg of its A row and of its
+// B row; the instructions only need A and B to assign K to (lane group, byte)
+// alike, which they do.  The output layout is that of the 16x16 SMFMAC, so
+// both ranges accumulate into the same registers.  fp8 has no dense 16x16
+// instruction taking 16 bytes a lane: two 8-byte ones (16x16x32) stand in.
+template <sp24_dtype DT>
+struct DenseHalf;
+template <>
+struct DenseHalf<SP24_BF16> {
+    __device__ static __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+};
+template <>
+struct DenseHalf<SP24_F16> {
+    __device__ static __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    }
+};
+template <>
+struct DenseHalf<SP24_I8> {
+    __device__ static __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        i32x4 ci = __builtin_bit_cast(i32x4, c);
+        ci = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), ci, 0,
+                                                   0, 0);
+        return __builtin_bit_cast(f32x4, ci);
+    }
+};
+template <>
+struct DenseHalf<SP24_E4M3> {
+    __device__ static __forceinline__ f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+        const long a0 = (long)(((uint64_t)a.y << 32) | a.x), a1 = (long)(((uint64_t)a.w << 32) | a.z);
+        const long b0 = (long)(((uint64_t)b.y << 32) | b.x), b1 = (long)(((uint64_t)b.w << 32) | b.z);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, c, 0, 0, 0);
+    }
+};
+
 // One output tile of the GEMM, D[a][b] for a in [a0, a0 + rows), b in
 // [b0, b0 + TL::BB), over the whole K.  DENSE == false: A is compressed
 // (values + metadata), tile rows TL::BA.  DENSE == true: A is dense and the
@@ -104,12 +146,18 @@ __device__ __forceinline__ void split_halves(const uint4& q0, const uint4& q1, u
 // constant positions.  The pipeline, the B side and the epilogue are the same.
 // Y, sa and RA refer to this tile's region of A rows; `group` is the tile's
 // group of tile-sharing workgroups (it sets the K rotation).
-template <sp24_dtype DT, sp24_dtype OUT, class TL, bool DENSE>
+// KSPLIT: A's rows continue past the compressed range [0, K) with a dense
+// range of KD more columns (ad: RA x KD, row-major), which B's rows (K + KD
+// long) continue alike; after the compressed steps the tile runs the dense
+// range in 64-byte half steps into the same accumulators.
+template <sp24_dtype DT, sp24_dtype OUT, class TL, bool DENSE, bool KSPLIT = false>
 __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* msb,
                                           const uint8_t* __restrict__ av, const uint32_t* __restrict__ am,
                                           const uint8_t* __restrict__ B, const float* __restrict__ sa,
                                           const float* __restrict__ sb, void* __restrict__ Y, int RA, int RB,
-                                          int64_t K, int64_t sya, int64_t syb, int a0, int b0, int group) {
+                                          int64_t K, int64_t sya, int64_t syb, int a0, int b0, int group,
+                                          const uint8_t* __restrict__ ad = nullptr, int64_t KD = 0) {
+    static_assert(!(DENSE && KSPLIT), "a K-split tile has compressed rows");
     using L = StepLayout<DT>;
     using Op = SparseOp<DT>;
     constexpr int MWS = L::META_WORDS;                  // metadata words per row per step: 2 or 4
@@ -147,7 +195,7 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
 
     const int steps = (int)(K / L::KSTEP);
     const uint32_t a_row_bytes = (uint32_t)(DENSE ? K * L::ELEM : K / 2 * L::ELEM);
-    const uint32_t b_row_bytes = (uint32_t)(K * L::ELEM);
+    const uint32_t b_row_bytes = (uint32_t)((K + (KSPLIT ? KD : 0)) * L::ELEM);
     const uint32_t m_row_bytes = (uint32_t)(K / 8);
     const Buf bufA(av, (uint32_t)RA * a_row_bytes);     // rows past RA / RB read as zeros
     const Buf bufM(am, META ? (uint32_t)RA * m_row_bytes : 0u);
@@ -183,7 +231,7 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
     // slices through L2, while different groups spread over memory channels.
     // The rotation keeps metadata blocks aligned (a multiple of T), and is
     // dropped when the step count is not a multiple of T.
-    const int rot = steps % T ? 0 : (int)(((unsigned)group * 13u) % (unsigned)(steps / T)) * T;
+    const int rot = (steps == 0 || steps % T) ? 0 : (int)(((unsigned)group * 13u) % (unsigned)(steps / T)) * T;
     auto issue_part = [&](uint8_t* as, uint8_t* bs, uint8_t* ms, int sl, bool do_a, bool do_bm) {
         // step sl of the rotated K loop; steps past the end load nothing useful
         int s = sl + rot;
@@ -319,6 +367,82 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
         }
     }
     wait_vmcnt<0>();   // drain the (useless) loads of steps past the end
+
+    if constexpr (KSPLIT) {
+        // ---- the dense K range: half steps of HB bytes of every A and B row, through the same
+        // three stages (A: BA rows x HB, the whole A stage; B: BB rows x HB, the first half of a B
+        // stage), two half steps in flight, one barrier per half step; the 16-byte chunks of a row
+        // XOR-swizzled by row as the compressed A rows are
+        constexpr int HB = 64;
+        constexpr int DA_BYTES = kBA * HB, DB_BYTES = kBB * HB;
+        static_assert(DA_BYTES == kAStage && DB_BYTES <= kBStage, "a dense half step fits the stages");
+        constexpr int DA_LOADS = DA_BYTES / 1024 / kWaves;
+        constexpr int DB_WAVES = DB_BYTES / 1024 < kWaves ? DB_BYTES / 1024 : kWaves;
+        constexpr int DB_LOADS = DB_BYTES / 1024 / DB_WAVES;
+        static_assert(DA_LOADS >= 1 && DA_LOADS * kWaves * 1024 == DA_BYTES, "whole dense A loads per wave");
+        static_assert(DB_LOADS * DB_WAVES * 1024 == DB_BYTES, "whole dense B loads");
+        const int dsteps = (int)(KD * L::ELEM / HB);
+        const uint32_t ad_row_bytes = (uint32_t)(KD * L::ELEM);
+        const Buf bufD(ad, (uint32_t)RA * ad_row_bytes);   // rows past RA read as zeros
+        uint32_t gd[DA_LOADS], gbd[DB_LOADS];
+#pragma unroll
+        for (int j = 0; j < DA_LOADS; ++j) {
+            const int row = 16 * (DA_LOADS * wave + j) + lane / 4;
+            gd[j] = (uint32_t)(a0 + row) * ad_row_bytes + 16 * ((lane & 3) ^ ((row >> 1) & 3));
+        }
+        const int wb_ld = min(wave, DB_WAVES - 1);
+#pragma unroll
+        for (int j = 0; j < DB_LOADS; ++j) {
+            const int row = 16 * (DB_LOADS * wb_ld + j) + lane / 4;
+            gbd[j] = (uint32_t)(b0 + row) * b_row_bytes + (uint32_t)(K * L::ELEM) + 16 * ((lane & 3) ^ ((row >> 1) & 3));
+        }
+        const int drot = dsteps > 0 ? (int)(((unsigned)group * 13u) % (unsigned)dsteps) : 0;
+        auto dissue = [&](int st_, int hl) {
+            int h = hl + drot;
+            h = h >= dsteps ? h - dsteps : h;
+            const uint32_t so = hl < dsteps ? (uint32_t)h * HB : kOOB;
+#pragma unroll
+            for (int j = 0; j < DA_LOADS; ++j)
+                dma16(bufD, asb + st_ * kAStage + 1024 * (DA_LOADS * wave + j), gd[j], so);
+            if (wave < DB_WAVES) {
+#pragma unroll
+                for (int j = 0; j < DB_LOADS; ++j)
+                    dma16(bufB, bsb + st_ * kBStage + 1024 * (DB_LOADS * wave + j), gbd[j], so);
+            }
+        };
+        const int a_fr = (wa * 16 * kFA + r) * HB + 16 * (kg ^ ((r >> 1) & 3));
+        const int b_fr = (wb * 16 * kFB + r) * HB + 16 * (kg ^ ((r >> 1) & 3));
+        // every wave is done reading the stages of the compressed range
+        __syncthreads();
+        if (dsteps > 0) {
+            dissue(0, 0);
+            dissue(1, 1);
+        }
+        int dst = 0;
+        for (int hs = 0; hs < dsteps; ++hs) {
+            if (wave < DB_WAVES)
+                wait_vmcnt_lgkm0<DA_LOADS + DB_LOADS>();
+            else
+                wait_vmcnt_lgkm0<DA_LOADS>();
+            __builtin_amdgcn_s_barrier();
+            dissue(dst == 0 ? 2 : dst - 1, hs + 2);
+            const uint8_t* as = asb + dst * kAStage;
+            const uint8_t* bs = bsb + dst * kBStage;
+            uint4 fb[kFB];
+#pragma unroll
+            for (int j = 0; j < kFB; ++j)
+                fb[j] = *reinterpret_cast<const uint4*>(bs + b_fr + j * 16 * HB);
+#pragma unroll
+            for (int i = 0; i < kFA; ++i) {
+                const uint4 fa_ = *reinterpret_cast<const uint4*>(as + a_fr + i * 16 * HB);
+#pragma unroll
+                for (int j = 0; j < kFB; ++j)
+                    acc[i][j] = DenseHalf<DT>::mma(fa_, fb[j], acc[i][j]);
+            }
+            dst = dst == 2 ? 0 : dst + 1;
+        }
+        wait_vmcnt<0>();
+    }
 
     // ---- epilogue: fragment (i, j), lane -> D[a][b], a = .. + 4*kg + q, b = .. + r
     auto value = [&](int i, int j, int ar, int br) {
@@ -570,6 +694,44 @@ sp24_hybrid_tail(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am
     }
 }
 
+// The K-split hybrid GEMM: every tile runs the compressed K range of its
+// weight rows and then their dense K range, into one set of accumulators
+// (tile_body's KSPLIT form).  A = W (rows RA = N), B = X (rows RB = M).
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
+__global__ void __launch_bounds__(TL::THREADS, TL::OCC)
+sp24_ksplit(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const uint8_t* __restrict__ ad,
+            const uint8_t* __restrict__ B, const float* __restrict__ sa, const float* __restrict__ sb,
+            void* __restrict__ Y, int RA, int RB, int64_t KS, int64_t KD, int64_t sya, int64_t syb, int tiles_a,
+            int tiles_b) {
+    SP24_TILE_LDS(TL);
+    const TilePos p = tile_pos(xcd_order(gridDim.x), tiles_a, tiles_b);
+    tile_body<DT, OUT, TL, false, true>(asb, bsb, msb, av, am, B, sa, sb, Y, RA, RB, KS, sya, syb,
+                                        p.ta * TL::BA, p.tb * TL::BB, p.group, ad, KD);
+}
+
+// The K-split grid with a short last round, split into quarter tiles as
+// sp24_big_tail splits the plain one.
+template <sp24_dtype DT, sp24_dtype OUT>
+__global__ void __launch_bounds__(T256x256::THREADS, 1)
+sp24_ksplit_tail(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const uint8_t* __restrict__ ad,
+                 const uint8_t* __restrict__ B, const float* __restrict__ sa, const float* __restrict__ sb,
+                 void* __restrict__ Y, int RA, int RB, int64_t KS, int64_t KD, int64_t sya, int64_t syb,
+                 int tiles_a, int tiles_b, int n_big) {
+    SP24_TILE_LDS(T256x256);
+    const int b = (int)blockIdx.x;
+    if (b < n_big) {
+        const TilePos p = tile_pos(xcd_order_of(b, n_big), tiles_a, tiles_b);
+        tile_body<DT, OUT, T256x256, false, true>(asb, bsb, msb, av, am, B, sa, sb, Y, RA, RB, KS, sya, syb,
+                                                  p.ta * 256, p.tb * 256, p.group, ad, KD);
+    } else {
+        const int q = xcd_order_of(b - n_big, (int)gridDim.x - n_big);
+        const TilePos p = tile_pos(n_big + q / 4, tiles_a, tiles_b);
+        tile_body<DT, OUT, T128x128, false, true>(asb, bsb, msb, av, am, B, sa, sb, Y, RA, RB, KS, sya, syb,
+                                                  p.ta * 256 + 128 * ((q >> 1) & 1), p.tb * 256 + 128 * (q & 1),
+                                                  p.group, ad, KD);
+    }
+}
+
 template <sp24_dtype DT, sp24_dtype OUT, class TL>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s, const char** kname, const char* name) {
     const int RA = (int)(g.a_is_w ? g.N : g.M);
@@ -613,39 +775,93 @@ inline bool prefer_256(int64_t t256, int64_t t128, int64_t cus) {
 }
 
 template <class TL>
-int64_t tiles_of(const GemmArgs& g) {
-    const int64_t RA = g.a_is_w ? g.N : g.M, RB = g.a_is_w ? g.M : g.N;
+int64_t tiles_rc(int64_t RA, int64_t RB) {
     return ((RA + TL::BA - 1) / TL::BA) * ((RB + TL::BB - 1) / TL::BB) * TL::OCC;
 }
+
+// Which tile grid runs an RA x RB output.
+enum TileKind { kT256, kT256Tail, kT256x128, kT128x128, kT128x64, kT256x64 };
+struct TilePlan {
+    TileKind kind;
+    int64_t n_big, n_split;   // kT256Tail: whole 256 x 256 tiles, and tiles split into quarters
+};
 
 // The largest tile that keeps most CUs busy (measured: 256 x 256 from 192
 // tiles on); failing that, the smallest.  The smaller tiles run two
 // workgroups per CU.  A 256 x 256 grid of more than one round whose last
 // round would fill at most a quarter of the chip runs that round as quarter
 // tiles (sp24_big_tail).
-template <sp24_dtype DT, sp24_dtype OUT>
-hipError_t launch_big(const GemmArgs& g, hipStream_t s, const char** kname) {
-    const int64_t RB = g.a_is_w ? g.M : g.N;
+inline TilePlan plan_tiles(int64_t RA, int64_t RB) {
     constexpr int64_t kFill = 192;
     constexpr int64_t kCUs = 256;   // compute units of the gfx950 parts (MI350X, MI355X)
     if (RB > 64) {
-        const int64_t t256 = tiles_of<T256x256>(g), rest = t256 % kCUs;
+        const int64_t t256 = tiles_rc<T256x256>(RA, RB), rest = t256 % kCUs;
         // past one round: a remainder whose quarters fill at most one round goes
         // to quarter tiles (measured: 20-32% faster at remainders of 16 and 64
         // tiles; at 128, two rounds of quarters, -1% bf16 to +2.5% fp8)
-        if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs) return launch_tail<DT, OUT>(g, s, kname, t256 - rest, rest);
-        const int64_t t128 = tiles_of<T256x128>(g);
-        if (t256 >= kFill || (t128 >= kFill && prefer_256(t256, t128, kCUs)))
-            return launch_tile<DT, OUT, T256x256>(g, s, kname, "sp24_big_256x256");
-        if (t128 >= kFill) return launch_tile<DT, OUT, T256x128>(g, s, kname, "sp24_big_256x128");
+        if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs) return {kT256Tail, t256 - rest, rest};
+        const int64_t t128 = tiles_rc<T256x128>(RA, RB);
+        if (t256 >= kFill || (t128 >= kFill && prefer_256(t256, t128, kCUs))) return {kT256, 0, 0};
+        if (t128 >= kFill) return {kT256x128, 0, 0};
         // 128 x 128 tiles while they alone keep most CUs busy; fewer, the
         // 128 x 64 ones (measured: 14-19% faster at 128 tiles of 128 x 128)
-        if (tiles_of<T128x128>(g) / T128x128::OCC >= kFill)
-            return launch_tile<DT, OUT, T128x128>(g, s, kname, "sp24_big_128x128");
-        return launch_tile<DT, OUT, T128x64>(g, s, kname, "sp24_big_128x64");
+        if (tiles_rc<T128x128>(RA, RB) / T128x128::OCC >= kFill) return {kT128x128, 0, 0};
+        return {kT128x64, 0, 0};
     }
-    if (tiles_of<T256x64>(g) >= kFill) return launch_tile<DT, OUT, T256x64>(g, s, kname, "sp24_big_256x64");
-    return launch_tile<DT, OUT, T128x64>(g, s, kname, "sp24_big_128x64");
+    if (tiles_rc<T256x64>(RA, RB) >= kFill) return {kT256x64, 0, 0};
+    return {kT128x64, 0, 0};
+}
+
+template <sp24_dtype DT, sp24_dtype OUT>
+hipError_t launch_big(const GemmArgs& g, hipStream_t s, const char** kname) {
+    const int64_t RA = g.a_is_w ? g.N : g.M, RB = g.a_is_w ? g.M : g.N;
+    const TilePlan p = plan_tiles(RA, RB);
+    switch (p.kind) {
+    case kT256Tail: return launch_tail<DT, OUT>(g, s, kname, p.n_big, p.n_split);
+    case kT256: return launch_tile<DT, OUT, T256x256>(g, s, kname, "sp24_big_256x256");
+    case kT256x128: return launch_tile<DT, OUT, T256x128>(g, s, kname, "sp24_big_256x128");
+    case kT128x128: return launch_tile<DT, OUT, T128x128>(g, s, kname, "sp24_big_128x128");
+    case kT256x64: return launch_tile<DT, OUT, T256x64>(g, s, kname, "sp24_big_256x64");
+    default: return launch_tile<DT, OUT, T128x64>(g, s, kname, "sp24_big_128x64");
+    }
+}
+
+template <sp24_dtype DT, sp24_dtype OUT, class TL>
+hipError_t launch_ksplit_tile(const KsplitArgs& k, hipStream_t s, const char** kname, const char* name) {
+    const int RA = (int)k.N, RB = (int)k.M;
+    const int tiles_a = (RA + TL::BA - 1) / TL::BA, tiles_b = (RB + TL::BB - 1) / TL::BB;
+    if (kname)
+        *kname = name;
+    if (k.dry)
+        return hipSuccess;
+    hipLaunchKernelGGL((sp24_ksplit<DT, OUT, TL>), dim3(tiles_a * tiles_b), dim3(TL::THREADS), 0, s,
+                       (const uint8_t*)k.ws_vals, k.ws_meta, (const uint8_t*)k.wd, (const uint8_t*)k.x, k.scale_w,
+                       k.scale_x, k.Y, RA, RB, k.KS, k.K - k.KS, (int64_t)1, k.N, tiles_a, tiles_b);
+    return hipGetLastError();
+}
+
+template <sp24_dtype DT, sp24_dtype OUT>
+hipError_t launch_ksplit_tiles(const KsplitArgs& k, hipStream_t s, const char** kname) {
+    const TilePlan p = plan_tiles(k.N, k.M);
+    switch (p.kind) {
+    case kT256Tail: {
+        const int RA = (int)k.N, RB = (int)k.M;
+        if (kname)
+            *kname = "sp24_ksplit_256x256_tail";
+        if (k.dry)
+            return hipSuccess;
+        hipLaunchKernelGGL((sp24_ksplit_tail<DT, OUT>), dim3((unsigned)(p.n_big + 4 * p.n_split)),
+                           dim3(T256x256::THREADS), 0, s, (const uint8_t*)k.ws_vals, k.ws_meta,
+                           (const uint8_t*)k.wd, (const uint8_t*)k.x, k.scale_w, k.scale_x, k.Y, RA, RB, k.KS,
+                           k.K - k.KS, (int64_t)1, k.N, (RA + 255) / 256, (RB + 255) / 256, (int)p.n_big);
+        return hipGetLastError();
+    }
+    case kT256: return launch_ksplit_tile<DT, OUT, T256x256>(k, s, kname, "sp24_ksplit_256x256");
+    case kT256x128: return launch_ksplit_tile<DT, OUT, T256x128>(k, s, kname, "sp24_ksplit_256x128");
+    case kT128x128: return launch_ksplit_tile<DT, OUT, T128x128>(k, s, kname, "sp24_ksplit_128x128");
+    case kT256x64: return launch_ksplit_tile<DT, OUT, T256x64>(k, s, kname, "sp24_ksplit_256x64");
+    default: return launch_ksplit_tile<DT, OUT, T128x64>(k, s, kname, "sp24_ksplit_128x64");
+    }
 }
 
 template <sp24_dtype DT, sp24_dtype OUT, class TL>
@@ -729,6 +945,27 @@ hipError_t launch_sp24_gemm_big(const GemmArgs& g, hipStream_t s, const char** k
     case SP24_I8:
         if (g.out_dt == SP24_BF16) return launch_big<SP24_I8, SP24_BF16>(g, s, kname);
         return launch_big<SP24_I8, SP24_F32>(g, s, kname);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_sp24_ksplit(const KsplitArgs& k, hipStream_t s, const char** kname) {
+    switch (k.in_dt) {
+    case SP24_BF16:
+        if (k.out_dt == SP24_BF16) return launch_ksplit_tiles<SP24_BF16, SP24_BF16>(k, s, kname);
+        if (k.out_dt == SP24_F16) return launch_ksplit_tiles<SP24_BF16, SP24_F16>(k, s, kname);
+        return launch_ksplit_tiles<SP24_BF16, SP24_F32>(k, s, kname);
+    case SP24_F16:
+        if (k.out_dt == SP24_F16) return launch_ksplit_tiles<SP24_F16, SP24_F16>(k, s, kname);
+        if (k.out_dt == SP24_BF16) return launch_ksplit_tiles<SP24_F16, SP24_BF16>(k, s, kname);
+        return launch_ksplit_tiles<SP24_F16, SP24_F32>(k, s, kname);
+    case SP24_E4M3:
+        if (k.out_dt == SP24_BF16) return launch_ksplit_tiles<SP24_E4M3, SP24_BF16>(k, s, kname);
+        return launch_ksplit_tiles<SP24_E4M3, SP24_F32>(k, s, kname);
+    case SP24_I8:
+        if (k.out_dt == SP24_BF16) return launch_ksplit_tiles<SP24_I8, SP24_BF16>(k, s, kname);
+        return launch_ksplit_tiles<SP24_I8, SP24_F32>(k, s, kname);
     default:
         return hipErrorInvalidValue;
     }

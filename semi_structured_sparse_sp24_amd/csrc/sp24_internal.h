@@ -75,6 +75,23 @@ struct HybridArgs {
 };
 hipError_t launch_sp24_hybrid(const HybridArgs& h, hipStream_t s, const char** kname);
 
+// The K-split hybrid GEMM: Y (M x N) = X * W^T with W's columns [0, KS)
+// compressed (ws_vals N x KS/2, ws_meta N x KS/32) and [KS, K) dense (wd,
+// N x (K - KS)); one launch, both ranges into the same accumulators.
+struct KsplitArgs {
+    sp24_dtype in_dt, out_dt;
+    int64_t M, N, KS, K;
+    const void* ws_vals;
+    const uint32_t* ws_meta;
+    const void* wd;
+    const void* x;            // M x K
+    const float* scale_x;     // M, or null
+    const float* scale_w;     // N, or null
+    void* Y;
+    bool dry = false;
+};
+hipError_t launch_sp24_ksplit(const KsplitArgs& k, hipStream_t s, const char** kname);
+
 struct DenseArgs {
     sp24_dtype in_dt, out_dt;
     int64_t M, N, K;

@@ -305,3 +305,30 @@ def test_int8_dtype_rules():
     assert sp.gemm_kernel(True, sp.SPARSE_W, i8, bf, 4, 4096, 64) is None
     # prune+compress accepts int8 (any alignment, a general kernel takes the rest)
     assert sp.lib().sp24_prune_compress(sp.I8, 0, 64, None, 64, None, None, None) == 0
+
+
+def test_ksplit_validation_precedes_hip():
+    f = sp.lib().sp24_ksplit_gemm
+    ok = dict(dt=sp.BF16, out=sp.BF16, M=4, N=16, KS=256, K=512, v=16, m=32, wd=48, x=64, sx=None, sw=None, y=80)
+
+    def h(**kw):
+        a = {**ok, **kw}
+        return f(a["dt"], a["out"], a["M"], a["N"], a["KS"], a["K"], a["v"], a["m"], a["wd"], a["x"], a["sx"],
+                 a["sw"], a["y"], None)
+    assert h(dt=sp.F32) == 3 and h(dt=sp.E4M3, out=sp.F16) == 3 and h(dt=9) == 3
+    assert h(M=-1) == 2 and h(N=-1) == 2 and h(KS=-256) == 2 and h(KS=768) == 2 and h(K=510) == 2
+    assert h(M=0) == 0 and h(N=0) == 0
+    assert h(y=None) == 1 and h(x=None) == 1 and h(v=None) == 1 and h(m=None) == 1 and h(wd=None) == 1
+    assert h(KS=0, v=None, m=None) != 1 and h(KS=512, wd=None) != 1      # an empty range needs no pointer
+    assert h(K=480) == 4 and h(dt=sp.E4M3, K=448, KS=256) == 4            # whole K steps
+    assert h(KS=128) == 4                                                  # the 2:4 range in 256-column blocks
+    assert h(x=72) == 4 and h(wd=56) == 4 and h(y=88) == 4 and h(sw=66) == 4 and h(v=24) == 4
+    k = sp.ksplit_kernel
+    bf = __import__("torch").bfloat16
+    assert k(bf, bf, 4096, 4096, 3072, 4096) == "sp24_ksplit_256x256"
+    assert k(bf, bf, 2048, 3072, 2048, 4096) == "sp24_ksplit_256x128"
+    assert k(bf, bf, 64, 49152, 256, 4096) == "sp24_ksplit_256x64"
+    assert k(bf, bf, 16, 4096, 256, 512) == "sp24_ksplit_128x64"
+    assert k(bf, bf, 8192, 4352, 3072, 4096) == "sp24_ksplit_256x256_tail"     # 544 = 2 x 256 + 32 tiles
+    assert k(bf, bf, 0, 16, 256, 512) == "none" and k(bf, bf, 4, 16, 0, 0) == "fill_zero"
+    assert k(bf, bf, 4, 16, 128, 512) is None and k(bf, bf, 4, 16, 768, 512) is None
