@@ -61,7 +61,7 @@ using T256x64 = Tile<256, 64, 4, 2, 1>;
 using T128x64 = Tile<128, 64, 4, 2, 2>;
 
 __device__ __forceinline__ void dma16(const Buf& b, void* lds_base, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_void*)lds_base, 16, (int)voff, (int)soff, 0, 0);
+    dma16_lds(b, lds_base, voff, soff);
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits [3:0] and

@@ -45,8 +45,14 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 struct Buf {
     __amdgpu_buffer_rsrc_t r;
+    u32x4 d;   // the same descriptor as four scalar words, for the LDS DMA load below
     __device__ __forceinline__ Buf(const void* p, uint32_t bytes)
-        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000)) {}
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000)) {
+        const uint64_t a = (uint64_t)(uintptr_t)p;
+        d = (u32x4){(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) & 0xffffu,
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+    }
     __device__ __forceinline__ uint4 ld16(uint32_t off) const {
         u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
         return make_uint4(v[0], v[1], v[2], v[3]);
@@ -55,6 +61,31 @@ struct Buf {
         return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
     }
 };
+
+// Global -> LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane
+// l's 16 bytes at byte offset voff + soff of the buffer land at LDS address
+// lds + 16 l.  Rows past the buffer's size read as zeros.
+//
+// Written as inline assembly, not with the compiler's LDS-DMA builtin, on
+// purpose: the compiler cannot tell which LDS bytes a DMA load writes, so
+// before every LDS read that follows one it waits for every DMA load still in
+// flight (s_waitcnt vmcnt(0)), including those that fill later pipeline
+// stages, which drains the software pipeline at every step.  The kernels
+// order their DMA loads and LDS reads themselves: each waits with an explicit
+// s_waitcnt vmcnt(n) for its own loads of a stage, and a barrier then makes
+// every wave's loads of that stage visible before any wave reads it.  The
+// instruction has no register results (nothing to wait on for registers).
+// M0 holds the LDS address; gfx9 needs one wait state between writing M0 and
+// an LDS DMA load that reads it (the s_nop).
+__device__ __forceinline__ void dma16_lds(const Buf& b, void* lds, uint32_t voff, uint32_t soff) {
+    typedef __attribute__((address_space(3))) void lds_t;
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_t*)lds);
+    const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(b.d), "s"(so), "s"(m)
+                 : "m0");
+}
 
 template <sp24_dtype DT>
 struct SparseOp;
