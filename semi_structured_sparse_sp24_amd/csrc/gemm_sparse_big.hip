@@ -354,7 +354,7 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             wait_step((u + 1) % T == 0);
-            __builtin_amdgcn_s_barrier();
+            barrier_lds();
             const int x2 = u + 2;   // issued now: position within the unrolled block
             const int st2 = st == 0 ? 2 : st - 1;   // (s + u + 2) % 3
             uint8_t* const nms = x2 % T ? nullptr : ms_(blk + x2 / T);
@@ -424,7 +424,7 @@ __device__ __forceinline__ void tile_body(uint8_t* asb, uint8_t* bsb, uint8_t* m
                 wait_vmcnt_lgkm0<DA_LOADS + DB_LOADS>();
             else
                 wait_vmcnt_lgkm0<DA_LOADS>();
-            __builtin_amdgcn_s_barrier();
+            barrier_lds();
             dissue(dst == 0 ? 2 : dst - 1, hs + 2);
             const uint8_t* as = asb + dst * kAStage;
             const uint8_t* bs = bsb + dst * kBStage;

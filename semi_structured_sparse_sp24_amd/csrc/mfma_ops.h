@@ -87,6 +87,14 @@ __device__ __forceinline__ void dma16_lds(const Buf& b, void* lds, uint32_t voff
                  : "m0");
 }
 
+// s_barrier, then a compiler fence: the DMA loads above are invisible to the
+// compiler as LDS writes, so without the fence it may hoist LDS reads of the
+// next stage above the barrier that makes that stage's data visible.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <sp24_dtype DT>
 struct SparseOp;
 
