@@ -140,23 +140,23 @@ __device__ __forceinline__ void dense_tile(uint8_t* a0s, uint8_t* a1s, uint8_t* 
         gb[j] = (uint32_t)(b0 + row) * row_bytes + cb[j];
     }
     const int rot = (int)(((unsigned)group * 13u) % (unsigned)steps);
+    // The step's byte offset goes in the (uniform) scalar offset, kOOB for the
+    // padded steps past the end.  A lane whose chunk lies past the end of its
+    // row (the partial last step) moves its vector offset to kOOB instead,
+    // which with any scalar offset of a row is past the operand's size
+    // (< 2 GiB), so it reads zeros.  Both offsets are never kOOB at once (their
+    // sum would wrap).
     auto issue = [&](uint8_t* as, uint8_t* bs, int sl) {
         int s = sl + rot;
         s = s >= steps ? s - steps : s;
         const bool live = sl < steps;
-        const uint32_t so = (uint32_t)s * 128;
+        const uint32_t so = live ? (uint32_t)s * 128 : kOOB;
 #pragma unroll
-        for (int j = 0; j < LA; ++j) {
-            const bool in = live && so + ca[j] < row_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufW.r, (lds_void*)(as + 1024 * (LA * wave + j)), 16,
-                                                     (int)(in ? ga[j] : kOOB), (int)(in ? so : 0u), 0, 0);
-        }
+        for (int j = 0; j < LA; ++j)
+            dma16_lds(bufW, as + 1024 * (LA * wave + j), !live || so + ca[j] < row_bytes ? ga[j] : kOOB, so);
 #pragma unroll
-        for (int j = 0; j < LB; ++j) {
-            const bool in = live && so + cb[j] < row_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(bufX.r, (lds_void*)(bs + 1024 * (LB * wave + j)), 16,
-                                                     (int)(in ? gb[j] : kOOB), (int)(in ? so : 0u), 0, 0);
-        }
+        for (int j = 0; j < LB; ++j)
+            dma16_lds(bufX, bs + 1024 * (LB * wave + j), !live || so + cb[j] < row_bytes ? gb[j] : kOOB, so);
     };
 
     f32x16 acc[kFA][kFB];
@@ -197,11 +197,11 @@ __device__ __forceinline__ void dense_tile(uint8_t* a0s, uint8_t* a1s, uint8_t* 
     const int steps2 = (steps + 1) / 2 * 2;
     for (int s = 0; s < steps2; s += 2) {
         wait_vmcnt_lgkm0<0>();
-        __builtin_amdgcn_s_barrier();
+        barrier_lds();
         issue(a1s, b1s, s + 1);
         compute(a0s, b0s);
         wait_vmcnt_lgkm0<0>();
-        __builtin_amdgcn_s_barrier();
+        barrier_lds();
         issue(a0s, b0s, s + 2);
         compute(a1s, b1s);
     }
