@@ -13,12 +13,14 @@ timed with HIP events on the stream it runs on (time per launch = chain time
 through copies of the weights totalling 640 MiB, so every launch reads its
 operands from HBM as successive layers do; compute-bound ones run warm on one
 copy.  After the timed steps the per-shape tactic (sparse iff faster) is
-selected, the vendor dense GEMM (torch.nn.functional.linear, hipBLASLt) is
-timed on the bf16 shapes as context, and the CPU oracle is timed on the host
+selected, the vendor dense GEMM (torch.mm, hipBLASLt) is timed on the bf16
+shapes in chains like the library's, and the CPU oracle is timed on the host
 cores.  On the bf16 workloads, whose four shapes are the projections of a
 Llama-3-8B-like block, the tactic records also give the layer-level audit
 manifest of 32 such blocks per M (its metrics in the line; --manifest-dir
-writes it whole).
+writes it whole), once against the library's dense GEMM and once with the
+same decision rule against the vendor dense GEMM ("audit_vs_vendor_dense":
+sparse only where it beats both).
 
 With no --workload (or --workload all) every workload runs in this process:
 prefill first, the headline (its K timed steps after W warmup steps set
@@ -349,17 +351,19 @@ class Runner:
         return out
 
 
-def layer_audit(workload, w, records, manifest_dir):
+def layer_audit(workload, w, records, manifest_dir, tag="",
+                time_note="each layer at its selected path's warm median from the tactic record"):
     """The layer-level manifest of a Llama-3-8B-like stack (32 blocks of the four projections
     whose shapes the bf16 workloads time), one per M, from the tactic records of this run:
     its metrics go into the bench line, the whole manifest into manifest_dir if given."""
     shapes = sorted(tuple(x) for x in w["shapes"])
     if not records or shapes != sorted((N, K) for _, N, K in audit.LLAMA3_8B_BLOCK):
         return None
+    if any((N, K, M) not in records for M in w["ms"] for _, N, K in audit.LLAMA3_8B_BLOCK):
+        return None
     revision = audit.synthetic_revision(f"{workload}:{w['shapes']}:10000*c + 100*s + 10*t + j")
     out = {"model": f"Llama-3-8B-like: {audit.LLAMA3_8B_BLOCKS} blocks x (qkv, o, gate_up, down)",
-           "time": "each layer at its selected path's warm median from the tactic record; no time outside "
-                   "these layers (attention, norms) is counted",
+           "time": time_note + "; no time outside these layers (attention, norms) is counted",
            "per_M": {}}
     for M in w["ms"]:
         by_shape = {(N, K): records[(N, K, M)] for _, N, K in audit.LLAMA3_8B_BLOCK}
@@ -369,7 +373,8 @@ def layer_audit(workload, w, records, manifest_dir):
         out["per_M"][str(M)] = man["metrics"]
         if manifest_dir:
             os.makedirs(manifest_dir, exist_ok=True)
-            with open(os.path.join(manifest_dir, f"manifest_{workload}_M{M}.json"), "w") as f:
+            name = f"manifest_{workload}_M{M}" + (f"_{tag}" if tag else "") + ".json"
+            with open(os.path.join(manifest_dir, name), "w") as f:
                 json.dump(man, f, indent=1)
     return out
 
@@ -513,8 +518,9 @@ def cpu_baseline(workload, budget_s):
 
 def vendor_dense(workload, cases, steps=3):
     """The vendor dense GEMM (torch.mm, hipBLASLt) on the same dense pruned weights and
-    activations, timed as the library's chains are: context for the dense baseline, not part of
-    the step.  bf16 weight-compressed workloads only; microseconds per launch by case."""
+    activations, timed as the library's chains are: the dense side of the vendor-aware tactic,
+    not part of the step.  bf16 weight-compressed workloads only; per-launch microseconds of each
+    step (the first, untimed, dropped) by case."""
     if workload not in ("prefill", "decode"):
         return None
     w = inputs.WORKLOADS[workload]
@@ -532,7 +538,7 @@ def vendor_dense(workload, cases, steps=3):
         r.step()
     t = r.collect()
     r.release()
-    return {(key[1], key[2]): float(np.median(v[1:])) for key, v in t.items()}
+    return {(key[1], key[2]): [float(x) for x in v[1:]] for key, v in t.items()}
 
 
 def measure(workload, args, steps, warmup, cpu_budget, eager=False):
@@ -575,6 +581,7 @@ def measure(workload, args, steps, warmup, cpu_budget, eager=False):
 
     # ---------------------------------------------------------------- per-case table
     rows = []
+    vendor_records = {}
     tot = {"sparse_t": 0.0, "dense_t": 0.0, "flops": 0.0, "sparse_bytes": 0.0, "compress_t": 0.0,
            "compress_bytes": 0.0, "sparse_launches": 0}
     for c in cases:
@@ -608,9 +615,15 @@ def measure(workload, args, steps, warmup, cpu_budget, eager=False):
                    "t_sparse_p10_us": round(float(np.percentile(ts, 10)), 2),
                    "t_sparse_p90_us": round(float(np.percentile(ts, 90)), 2)}
             if vendor is not None:
-                tv = vendor[key]
+                tv = float(np.median(vendor[key]))
+                # the pages' rule with the fastest dense GEMM on this part as the dense side: the
+                # sparse path is selected only where it beats the vendor's dense GEMM as well
+                vrec = sp.tactic_decide(True, [float(x) for x in ts], vendor[key])
+                if vrec["selected"] == "dense":
+                    vrec["kernel"] = "hipBLASLt (torch.mm)"
+                vendor_records[(N, K, M)] = vrec
                 row.update(t_vendor_dense_us=round(tv, 2), speedup_vs_vendor_dense=round(tv / tsm, 3),
-                           own_dense_vs_vendor=round(tdm / tv, 3))
+                           own_dense_vs_vendor=round(tdm / tv, 3), selected_vs_vendor=vrec["selected"])
             if workload == HYBRID:
                 tsp = float(np.median(times[("split",) + key]))
                 row.update(N_s=c["NS"], N_d=c["ND"], t_two_launch_us=round(tsp, 2),
@@ -726,6 +739,11 @@ def measure(workload, args, steps, warmup, cpu_budget, eager=False):
                                 "reason": rec["reason"], "kernel": rec["kernel"]})
                 records[(N, K, M)] = rec
     audit_summary = layer_audit(workload, w, records, args.manifest_dir)
+    audit_vendor = layer_audit(workload, w, vendor_records, args.manifest_dir, tag="vs_vendor",
+                               time_note="each layer at its selected path's median per-launch time in this "
+                                         "run's bench chains (the step's cache mode)")
+    if audit_vendor is not None:
+        audit_vendor["dense_side"] = "hipBLASLt through torch.mm on the same pruned weights"
     del cases
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -750,6 +768,7 @@ def measure(workload, args, steps, warmup, cpu_budget, eager=False):
         "cases": rows,
         "tactics": tactics,
         "audit": audit_summary,
+        "audit_vs_vendor_dense": audit_vendor,
     }
     return result, wall
 
@@ -781,7 +800,7 @@ def compact(rec):
     """A non-headline workload's record in the line: the per-case table kept to its main columns."""
     keep = ("N", "K", "M", "N_s", "N_d", "K_s", "K_d", "t_sparse_us", "t_dense_us", "speedup", "sparse_tflops",
             "sparse_GBps", "sparse_hbm_frac", "sparse_mfma_frac", "t_compress_us", "speedup_incl_compress",
-            "t_two_launch_us", "t_vendor_dense_us")
+            "t_two_launch_us", "t_vendor_dense_us", "selected_vs_vendor")
     out = dict(rec)
     out["cases"] = [{k: v for k, v in r.items() if k in keep} for r in rec["cases"]]
     out["roofline"] = {k: v for k, v in rec["roofline"].items() if k != "kernels"}
@@ -805,7 +824,7 @@ def main():
                          "workload, 4 for each other workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tactic", action="store_true")
-    ap.add_argument("--no-vendor", action="store_true", help="skip the hipBLASLt context timing")
+    ap.add_argument("--no-vendor", action="store_true", help="skip the hipBLASLt timing and the vendor-aware audit")
     ap.add_argument("--manifest-dir", default=None,
                     help="write the layer-level audit manifest of each M there (bf16 workloads)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -853,6 +872,7 @@ def main():
         "speedup_vs_dense": h["speedup_vs_dense"], "compress_GBps": h["compress_GBps"],
         "compress_hbm_frac": h["compress_hbm_frac"], "roofline": h["roofline"], "cpu_baseline": h["cpu_baseline"],
         "cases": h["cases"], "tactics": h["tactics"], "audit": h["audit"],
+        "audit_vs_vendor_dense": h["audit_vs_vendor_dense"],
         "workloads": {n: compact(r) for n, r in records.items() if n != head},
         "versions": {"torch": torch.__version__, "hip": torch.version.hip, "lib": sp.version()},
     }
