@@ -317,13 +317,15 @@ dense_big(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const fl
 
 // The 256 x 256 grid with a short last round, as the sparse tile kernels run
 // it: the first n_big tiles (whole rounds) as 256 x 256, each later tile as
-// four 128 x 128 quarters, in the big tile's LDS.
+// `parts` smaller tiles (four 128 x 128 quarters, or two 256 x 128 halves),
+// in the big tile's LDS.
 template <sp24_dtype DT, sp24_dtype OUT>
 __global__ void __launch_bounds__(D256x256::THREADS, 1)
 dense_big_tail(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, const float* __restrict__ sx,
                const float* __restrict__ sw, void* __restrict__ Y, int N, int M, int64_t K, int tiles_a,
-               int tiles_b, int n_big) {
-    static_assert(D128x128::THREADS == D256x256::THREADS, "one block size");
+               int tiles_b, int n_big, int parts) {
+    static_assert(D128x128::THREADS == D256x256::THREADS && D256x128::THREADS == D256x256::THREADS,
+                  "one block size");
     __shared__ __attribute__((aligned(1024))) uint8_t a0s[256 * 128], a1s[256 * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t b0s[256 * 128], b1s[256 * 128];
     const int b = (int)blockIdx.x;
@@ -331,6 +333,12 @@ dense_big_tail(const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, con
         const DTilePos p = dtile_pos(dxcd_order(b, n_big), tiles_a, tiles_b);
         dense_tile<DT, OUT, D256x256>(a0s, a1s, b0s, b1s, W, X, sx, sw, Y, N, M, K, p.ta * 256, p.tb * 256,
                                       p.group);
+    } else if (parts == 2) {
+        // n_big is a multiple of 8, so b - n_big keeps b's XCD
+        const int q = dxcd_order(b - n_big, (int)gridDim.x - n_big);
+        const DTilePos p = dtile_pos(n_big + q / 2, tiles_a, tiles_b);
+        dense_tile<DT, OUT, D256x128>(a0s, a1s, b0s, b1s, W, X, sx, sw, Y, N, M, K, p.ta * 256,
+                                      p.tb * 256 + 128 * (q & 1), p.group);
     } else {
         // n_big is a multiple of 8, so b - n_big keeps b's XCD
         const int q = dxcd_order(b - n_big, (int)gridDim.x - n_big);
@@ -355,16 +363,17 @@ hipError_t launch_tile(const DenseArgs& g, hipStream_t s, const char** kname, co
 }
 
 template <sp24_dtype DT, sp24_dtype OUT>
-hipError_t launch_tail(const DenseArgs& g, hipStream_t s, const char** kname, int64_t n_big, int64_t n_split) {
+hipError_t launch_tail(const DenseArgs& g, hipStream_t s, const char** kname, int64_t n_big, int64_t n_split,
+                       int parts) {
     const int N = (int)g.N, M = (int)g.M;
     const int tiles_a = (N + 255) / 256, tiles_b = (M + 255) / 256;
     if (kname)
         *kname = "dense_big_256x256_tail";
     if (g.dry)
         return hipSuccess;
-    hipLaunchKernelGGL((dense_big_tail<DT, OUT>), dim3((unsigned)(n_big + 4 * n_split)), dim3(D256x256::THREADS), 0,
-                       s, (const uint8_t*)g.W, (const uint8_t*)g.X, g.scale_x, g.scale_w, g.Y, N, M, g.K, tiles_a,
-                       tiles_b, (int)n_big);
+    hipLaunchKernelGGL((dense_big_tail<DT, OUT>), dim3((unsigned)(n_big + parts * n_split)), dim3(D256x256::THREADS),
+                       0, s, (const uint8_t*)g.W, (const uint8_t*)g.X, g.scale_x, g.scale_w, g.Y, N, M, g.K, tiles_a,
+                       tiles_b, (int)n_big, parts);
     return hipGetLastError();
 }
 
@@ -375,14 +384,18 @@ int64_t tiles_of(const DenseArgs& g) {
 
 // The same tile choice as the sparse kernels: the largest tile that keeps
 // most CUs busy (192 workgroups), else the smallest; a short last round of
-// 256 x 256 tiles (at most a quarter of the chip) as quarter tiles.
+// 256 x 256 tiles as quarter tiles (at most a quarter of the chip) or half
+// tiles (at most half of it).
 template <sp24_dtype DT, sp24_dtype OUT>
 hipError_t launch(const DenseArgs& g, hipStream_t s, const char** kname) {
     constexpr int64_t kFill = 192;
     constexpr int64_t kCUs = 256;   // compute units of the gfx950 parts (MI350X, MI355X)
     if (g.M > 64) {
         const int64_t t256 = tiles_of<D256x256>(g), rest = t256 % kCUs;
-        if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs) return launch_tail<DT, OUT>(g, s, kname, t256 - rest, rest);
+        if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs)
+            return launch_tail<DT, OUT>(g, s, kname, t256 - rest, rest, 4);
+        if (t256 > kCUs && rest > 0 && 2 * rest <= kCUs)
+            return launch_tail<DT, OUT>(g, s, kname, t256 - rest, rest, 2);
         // between 256 x 256 and 256 x 128: the cheaper rounds, as the sparse kernels choose
         const int64_t t128 = tiles_of<D256x128>(g);
         const int64_t r256 = (t256 + kCUs - 1) / kCUs, r128 = (t128 + kCUs - 1) / kCUs;

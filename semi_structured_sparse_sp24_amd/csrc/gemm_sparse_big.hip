@@ -601,26 +601,36 @@ sp24_big(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const 
 
 // The 256 x 256 grid whose last round would leave most compute units idle:
 // the first n_big tiles (whole rounds of the chip) run as in sp24_big; each
-// later tile is split into four 128 x 128 tiles, so that the remainder takes
-// every compute unit for a shorter round instead of a few of them for a full
-// one.  Each output element is still computed by exactly one workgroup.  The
-// two ranges are ordered separately, so that the big tiles are dispatched
-// first; the four quarters of a tile are consecutive in the XCD-aware order
-// and share its operands through one XCD's L2.
+// later tile is split into `parts` smaller tiles -- four 128 x 128 quarters,
+// or two 256 x 128 halves (along B) -- so that the remainder takes every
+// compute unit for a shorter round instead of some of them for a full one.
+// Each output element is still computed by exactly one workgroup.  The two
+// ranges are ordered separately, so that the big tiles are dispatched first;
+// the parts of a tile are consecutive in the XCD-aware order and share its
+// operands through one XCD's L2.
 template <sp24_dtype DT, sp24_dtype OUT>
 __global__ void __launch_bounds__(T256x256::THREADS, 1)
 sp24_big_tail(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const uint8_t* __restrict__ B,
               const float* __restrict__ sa, const float* __restrict__ sb, void* __restrict__ Y, int RA, int RB,
-              int64_t K, int64_t sya, int64_t syb, int tiles_a, int tiles_b, int n_big) {
-    static_assert(T128x128::THREADS == T256x256::THREADS, "one block size");
+              int64_t K, int64_t sya, int64_t syb, int tiles_a, int tiles_b, int n_big, int parts) {
+    static_assert(T128x128::THREADS == T256x256::THREADS && T256x128::THREADS == T256x256::THREADS,
+                  "one block size");
     static_assert(T128x128::A_STAGE <= T256x256::A_STAGE && T128x128::B_STAGE <= T256x256::B_STAGE &&
                       T128x128::M_BLOCK <= T256x256::M_BLOCK, "the quarter tiles use the big tile's LDS");
+    static_assert(T256x128::A_STAGE <= T256x256::A_STAGE && T256x128::B_STAGE <= T256x256::B_STAGE &&
+                      T256x128::M_BLOCK <= T256x256::M_BLOCK, "the half tiles use the big tile's LDS");
     SP24_TILE_LDS(T256x256);
     const int b = (int)blockIdx.x;
     if (b < n_big) {
         const TilePos p = tile_pos(xcd_order_of(b, n_big), tiles_a, tiles_b);
         tile_body<DT, OUT, T256x256, false>(asb, bsb, msb, av, am, B, sa, sb, Y, RA, RB, K, sya, syb,
                                             p.ta * 256, p.tb * 256, p.group);
+    } else if (parts == 2) {
+        // n_big is a multiple of 8, so b - n_big keeps b's XCD
+        const int q = xcd_order_of(b - n_big, (int)gridDim.x - n_big);
+        const TilePos p = tile_pos(n_big + q / 2, tiles_a, tiles_b);
+        tile_body<DT, OUT, T256x128, false>(asb, bsb, msb, av, am, B, sa, sb, Y, RA, RB, K, sya, syb,
+                                            p.ta * 256, p.tb * 256 + 128 * (q & 1), p.group);
     } else {
         // n_big is a multiple of 8, so b - n_big keeps b's XCD
         const int q = xcd_order_of(b - n_big, (int)gridDim.x - n_big);
@@ -709,20 +719,25 @@ sp24_ksplit(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, con
                                         p.ta * TL::BA, p.tb * TL::BB, p.group, ad, KD);
 }
 
-// The K-split grid with a short last round, split into quarter tiles as
-// sp24_big_tail splits the plain one.
+// The K-split grid with a short last round, split into quarter or half tiles
+// as sp24_big_tail splits the plain one.
 template <sp24_dtype DT, sp24_dtype OUT>
 __global__ void __launch_bounds__(T256x256::THREADS, 1)
 sp24_ksplit_tail(const uint8_t* __restrict__ av, const uint32_t* __restrict__ am, const uint8_t* __restrict__ ad,
                  const uint8_t* __restrict__ B, const float* __restrict__ sa, const float* __restrict__ sb,
                  void* __restrict__ Y, int RA, int RB, int64_t KS, int64_t KD, int64_t sya, int64_t syb,
-                 int tiles_a, int tiles_b, int n_big) {
+                 int tiles_a, int tiles_b, int n_big, int parts) {
     SP24_TILE_LDS(T256x256);
     const int b = (int)blockIdx.x;
     if (b < n_big) {
         const TilePos p = tile_pos(xcd_order_of(b, n_big), tiles_a, tiles_b);
         tile_body<DT, OUT, T256x256, false, true>(asb, bsb, msb, av, am, B, sa, sb, Y, RA, RB, KS, sya, syb,
                                                   p.ta * 256, p.tb * 256, p.group, ad, KD);
+    } else if (parts == 2) {
+        const int q = xcd_order_of(b - n_big, (int)gridDim.x - n_big);
+        const TilePos p = tile_pos(n_big + q / 2, tiles_a, tiles_b);
+        tile_body<DT, OUT, T256x128, false, true>(asb, bsb, msb, av, am, B, sa, sb, Y, RA, RB, KS, sya, syb,
+                                                  p.ta * 256, p.tb * 256 + 128 * (q & 1), p.group, ad, KD);
     } else {
         const int q = xcd_order_of(b - n_big, (int)gridDim.x - n_big);
         const TilePos p = tile_pos(n_big + q / 4, tiles_a, tiles_b);
@@ -749,7 +764,8 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t s, const char** kname, con
 }
 
 template <sp24_dtype DT, sp24_dtype OUT>
-hipError_t launch_tail(const GemmArgs& g, hipStream_t s, const char** kname, int64_t n_big, int64_t n_split) {
+hipError_t launch_tail(const GemmArgs& g, hipStream_t s, const char** kname, int64_t n_big, int64_t n_split,
+                       int parts) {
     const int RA = (int)(g.a_is_w ? g.N : g.M);
     const int RB = (int)(g.a_is_w ? g.M : g.N);
     const int64_t sya = g.a_is_w ? 1 : g.N, syb = g.a_is_w ? g.N : 1;
@@ -758,9 +774,9 @@ hipError_t launch_tail(const GemmArgs& g, hipStream_t s, const char** kname, int
         *kname = "sp24_big_256x256_tail";
     if (g.dry)
         return hipSuccess;
-    hipLaunchKernelGGL((sp24_big_tail<DT, OUT>), dim3((unsigned)(n_big + 4 * n_split)), dim3(T256x256::THREADS), 0, s,
-                       (const uint8_t*)g.a_vals, g.a_meta, (const uint8_t*)g.b, g.scale_a, g.scale_b, g.Y, RA, RB,
-                       g.K, sya, syb, tiles_a, tiles_b, (int)n_big);
+    hipLaunchKernelGGL((sp24_big_tail<DT, OUT>), dim3((unsigned)(n_big + parts * n_split)), dim3(T256x256::THREADS),
+                       0, s, (const uint8_t*)g.a_vals, g.a_meta, (const uint8_t*)g.b, g.scale_a, g.scale_b, g.Y, RA,
+                       RB, g.K, sya, syb, tiles_a, tiles_b, (int)n_big, parts);
     return hipGetLastError();
 }
 
@@ -783,15 +799,17 @@ int64_t tiles_rc(int64_t RA, int64_t RB) {
 enum TileKind { kT256, kT256Tail, kT256x128, kT128x128, kT128x64, kT256x64 };
 struct TilePlan {
     TileKind kind;
-    int64_t n_big, n_split;   // kT256Tail: whole 256 x 256 tiles, and tiles split into quarters
+    int64_t n_big, n_split;   // kT256Tail: whole 256 x 256 tiles, and the tiles split into parts
+    int parts;                // kT256Tail: 4 (128 x 128 quarters) or 2 (256 x 128 halves)
 };
 
 // The largest tile that keeps most CUs busy (measured: 256 x 256 from 192
 // tiles on); failing that, the smallest.  The smaller tiles run two
 // workgroups per CU.  A 256 x 256 grid of more than one round whose last
 // round would fill at most a quarter of the chip runs that round as quarter
-// tiles (sp24_big_tail).
-inline TilePlan plan_tiles(int64_t RA, int64_t RB) {
+// tiles (sp24_big_tail); with `halves`, one that would fill at most half of
+// it runs as half tiles.
+inline TilePlan plan_tiles(int64_t RA, int64_t RB, bool halves = false) {
     constexpr int64_t kFill = 192;
     constexpr int64_t kCUs = 256;   // compute units of the gfx950 parts (MI350X, MI355X)
     if (RB > 64) {
@@ -799,7 +817,8 @@ inline TilePlan plan_tiles(int64_t RA, int64_t RB) {
         // past one round: a remainder whose quarters fill at most one round goes
         // to quarter tiles (measured: 20-32% faster at remainders of 16 and 64
         // tiles; at 128, two rounds of quarters, -1% bf16 to +2.5% fp8)
-        if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs) return {kT256Tail, t256 - rest, rest};
+        if (t256 > kCUs && rest > 0 && 4 * rest <= kCUs) return {kT256Tail, t256 - rest, rest, 4};
+        if (halves && t256 > kCUs && rest > 0 && 2 * rest <= kCUs) return {kT256Tail, t256 - rest, rest, 2};
         const int64_t t128 = tiles_rc<T256x128>(RA, RB);
         if (t256 >= kFill || (t128 >= kFill && prefer_256(t256, t128, kCUs))) return {kT256, 0, 0};
         if (t128 >= kFill) return {kT256x128, 0, 0};
@@ -815,9 +834,9 @@ inline TilePlan plan_tiles(int64_t RA, int64_t RB) {
 template <sp24_dtype DT, sp24_dtype OUT>
 hipError_t launch_big(const GemmArgs& g, hipStream_t s, const char** kname) {
     const int64_t RA = g.a_is_w ? g.N : g.M, RB = g.a_is_w ? g.M : g.N;
-    const TilePlan p = plan_tiles(RA, RB);
+    const TilePlan p = plan_tiles(RA, RB, true);
     switch (p.kind) {
-    case kT256Tail: return launch_tail<DT, OUT>(g, s, kname, p.n_big, p.n_split);
+    case kT256Tail: return launch_tail<DT, OUT>(g, s, kname, p.n_big, p.n_split, p.parts);
     case kT256: return launch_tile<DT, OUT, T256x256>(g, s, kname, "sp24_big_256x256");
     case kT256x128: return launch_tile<DT, OUT, T256x128>(g, s, kname, "sp24_big_256x128");
     case kT128x128: return launch_tile<DT, OUT, T128x128>(g, s, kname, "sp24_big_128x128");
@@ -842,7 +861,7 @@ hipError_t launch_ksplit_tile(const KsplitArgs& k, hipStream_t s, const char** k
 
 template <sp24_dtype DT, sp24_dtype OUT>
 hipError_t launch_ksplit_tiles(const KsplitArgs& k, hipStream_t s, const char** kname) {
-    const TilePlan p = plan_tiles(k.N, k.M);
+    const TilePlan p = plan_tiles(k.N, k.M, true);
     switch (p.kind) {
     case kT256Tail: {
         const int RA = (int)k.N, RB = (int)k.M;
@@ -850,10 +869,10 @@ hipError_t launch_ksplit_tiles(const KsplitArgs& k, hipStream_t s, const char** 
             *kname = "sp24_ksplit_256x256_tail";
         if (k.dry)
             return hipSuccess;
-        hipLaunchKernelGGL((sp24_ksplit_tail<DT, OUT>), dim3((unsigned)(p.n_big + 4 * p.n_split)),
+        hipLaunchKernelGGL((sp24_ksplit_tail<DT, OUT>), dim3((unsigned)(p.n_big + p.parts * p.n_split)),
                            dim3(T256x256::THREADS), 0, s, (const uint8_t*)k.ws_vals, k.ws_meta,
                            (const uint8_t*)k.wd, (const uint8_t*)k.x, k.scale_w, k.scale_x, k.Y, RA, RB, k.KS,
-                           k.K - k.KS, (int64_t)1, k.N, (RA + 255) / 256, (RB + 255) / 256, (int)p.n_big);
+                           k.K - k.KS, (int64_t)1, k.N, (RA + 255) / 256, (RB + 255) / 256, (int)p.n_big, p.parts);
         return hipGetLastError();
     }
     case kT256: return launch_ksplit_tile<DT, OUT, T256x256>(k, s, kname, "sp24_ksplit_256x256");

@@ -136,10 +136,14 @@ def test_gemm_kernel_names_follow_the_dispatch():
     assert k(True, sp.SPARSE_W, bf, bf, 4096, 5120, 5120) == "sp24_big_256x256_tail"        # 320 = 256 + 64
     assert k(True, sp.SPARSE_W, bf, bf, 4096, 4352, 4096) == "sp24_big_256x256_tail"        # 272 = 256 + 16
     assert k(True, sp.SPARSE_X, bf, bf, 5120, 4096, 4096) == "sp24_big_256x256_tail"        # A = X: 20 x 16
-    assert k(True, sp.SPARSE_W, bf, bf, 2048, 28672, 4096) == "sp24_big_256x256"            # 896 = 3 * 256 + 128
+    # ... at most half of it: half tiles, in the same tail kernel
+    assert k(True, sp.SPARSE_W, bf, bf, 2048, 28672, 4096) == "sp24_big_256x256_tail"       # 896 = 3 * 256 + 128
+    assert k(True, sp.SPARSE_W, bf, bf, 4093, 5276, 4096) == "sp24_big_256x256_tail"        # 336 = 256 + 80
+    # more than half of it: a last round of whole tiles
+    assert k(True, sp.SPARSE_W, bf, bf, 4608, 28672, 4096) == "sp24_big_256x256"            # 2016 = 7 * 256 + 224
     assert k(True, sp.SPARSE_W, bf, bf, 2048, 6144, 4096) == "sp24_big_256x256"             # 192: one round
     assert k(False, sp.SPARSE_W, bf, bf, 4096, 5120, 5120) == "dense_big_256x256_tail"
-    assert k(False, sp.SPARSE_W, bf, bf, 2048, 28672, 4096) == "dense_big_256x256"
+    assert k(False, sp.SPARSE_W, bf, bf, 2048, 28672, 4096) == "dense_big_256x256_tail"
     # 160 tiles of 256x256 (one round) against 320 of 256x128 (two): the big ones
     assert k(True, sp.SPARSE_W, bf, bf, 2048, 5120, 4096) == "sp24_big_256x256"
     assert k(False, sp.SPARSE_W, bf, bf, 2048, 5120, 4096) == "dense_big_256x256"

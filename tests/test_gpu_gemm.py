@@ -284,15 +284,35 @@ def test_tail_quarter_tiles(dt, which, M, N, steps):
     into 128x128 quarter tiles: integer inputs, rows sampled from every
     256-row band of the output (both halves of each), bitwise equal to the
     oracle, and every output written."""
+    _tail_case(dt, which, M, N, steps, quarters=True)
+
+
+# remainders of 65 to 128 tiles, whose halves (256x128, split along B) fill
+# one round: (M, N, K steps) with ragged last tiles in both dimensions
+TAIL_HALVES = [(2048 - 7, 28672 - 40, 6), (4093, 5276, 7)]
+
+
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.E4M3])
+@pytest.mark.parametrize("which", ["sparse_w", "sparse_x", "dense"])
+@pytest.mark.parametrize("M,N,steps", TAIL_HALVES)
+def test_tail_half_tiles(dt, which, M, N, steps):
+    """The same with the last round split into 256x128 half tiles."""
+    _tail_case(dt, which, M, N, steps, quarters=False)
+
+
+def _tail_case(dt, which, M, N, steps, quarters):
     K = steps * (64 if dt != oracle.E4M3 else 128)
     RA, RB = (M, N) if which == "sparse_x" else (N, M)
     t = ((RA + 255) // 256) * ((RB + 255) // 256)
-    assert t > 256 and 0 < t % 256 <= 64, t
+    if quarters:
+        assert t > 256 and 0 < t % 256 <= 64, t
+    else:
+        assert t > 256 and 64 < t % 256 <= 128, t
     ttype = {oracle.BF16: torch.bfloat16, oracle.F16: torch.float16, oracle.E4M3: torch.float8_e4m3fn}[dt]
     op = sp.SPARSE_X if which == "sparse_x" else sp.SPARSE_W
     name = "dense_big_256x256_tail" if which == "dense" else "sp24_big_256x256_tail"
     assert sp.gemm_kernel(which != "dense", op, ttype, torch.float32, M, N, K) == name
-    say("tail quarters", which, dt, M, N, K)
+    say("tail quarters" if quarters else "tail halves", which, dt, M, N, K)
     xb, _, wb, _ = _operands(dt, M, N, K, 321, integer=True)
     rows = np.unique(np.clip(np.concatenate([np.arange(0, M, 256), np.arange(129, M, 256),
                                              np.arange(255, M, 256), [M - 1]]), 0, M - 1))

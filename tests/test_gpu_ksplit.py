@@ -72,11 +72,12 @@ def _run(dt, out, M, N, KS, K, seed, integer=False, rows=None):
 
 # (M, N, K_s, K): 128x64 tiles with ragged edges; 256x64 (M <= 64, wide N);
 # 128x128; 256x128; 256x256 with ragged N; the 256x256 grid with a quarter-tile
-# tail; a 2:4 range shorter than the dense one
+# tail (544 tiles = 2 * 256 + 32) and with a half-tile tail (336 = 256 + 80,
+# ragged in both dimensions); a 2:4 range shorter than the dense one
 CASES = [(40, 200, 256, 512), (64, 49408, 256, 512), (1600, 2048, 256, 1024), (2048, 3072, 768, 1024),
-         (2816, 4500, 512, 1024), (8192, 4352, 256, 512), (300, 520, 256, 1280)]
+         (2816, 4500, 512, 1024), (8192, 4352, 256, 512), (4093, 5276, 256, 512), (300, 520, 256, 1280)]
 KERNELS = ["sp24_ksplit_128x64", "sp24_ksplit_256x64", "sp24_ksplit_128x128", "sp24_ksplit_256x128",
-           "sp24_ksplit_256x256", "sp24_ksplit_256x256_tail", "sp24_ksplit_128x64"]
+           "sp24_ksplit_256x256", "sp24_ksplit_256x256_tail", "sp24_ksplit_256x256_tail", "sp24_ksplit_128x64"]
 
 
 def test_cases_cover_every_tile_shape():
