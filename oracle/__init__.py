@@ -69,6 +69,10 @@ def _load(path=None):
     lib.oracle_encode_e4m3.argtypes = [ctypes.c_double]
     lib.oracle_quantize_e4m3_rows.restype = i32
     lib.oracle_quantize_e4m3_rows.argtypes = [i32, i64, i64, vp, i64, vp, vp]
+    lib.oracle_encode_i8.restype = ctypes.c_int8
+    lib.oracle_encode_i8.argtypes = [ctypes.c_float]
+    lib.oracle_quantize_i8_rows.restype = i32
+    lib.oracle_quantize_i8_rows.argtypes = [i32, i64, i64, vp, i64, vp, vp]
     lib.oracle_gemm.restype = i32
     lib.oracle_gemm.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
     lib.oracle_audit.restype = i32
@@ -183,6 +187,31 @@ def quantize_prune_compress(dt: int, src: np.ndarray):
     and compress of the codes -> (values rows x K/2, meta, scales)."""
     q, scales = quantize_e4m3_rows(dt, src)
     values, meta = prune_compress(E4M3, q)
+    return values, meta, scales
+
+
+def encode_i8(t: float) -> int:
+    """The int8 code of an fp32 quotient (nearest, ties to even, saturated to +-127; NaN -> 0)."""
+    return int(_load().oracle_encode_i8(float(t)))
+
+
+def quantize_i8_rows(dt: int, src: np.ndarray):
+    """16-bit rows x K bit patterns -> (int8 codes rows x K as uint8 bytes, fp32 scale per row)."""
+    src = np.ascontiguousarray(src, dtype=_bits_dtype(dt))
+    rows, K = src.shape
+    q = np.empty((rows, K), dtype=np.uint8)
+    scales = np.empty(rows, dtype=np.float32)
+    rc = _load().oracle_quantize_i8_rows(dt, rows, K, _ptr(src), K, _ptr(q), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_i8_rows rejected dt={dt} shape={src.shape}")
+    return q, scales
+
+
+def quantize_i8_prune_compress(dt: int, src: np.ndarray):
+    """The fused online int8 path: per-row quantization to int8, then 2:4 prune
+    and compress of the codes -> (values rows x K/2, meta, scales)."""
+    q, scales = quantize_i8_rows(dt, src)
+    values, meta = prune_compress(I8, q)
     return values, meta, scales
 
 

@@ -42,7 +42,11 @@
  *     with per-row fp32 scales as for fp8;
  *   - fused online fp8 path: per-row scale max|x| / 448 and codes e4m3(x / s)
  *     rounded to nearest even and saturated at 448, both in fp32; pruning
- *     acts on the codes (quantize first, then prune).
+ *     acts on the codes (quantize first, then prune);
+ *   - fused online int8 path: per-row scale max|x| / 127 and codes
+ *     int8(x / s), the quotient rounded to the nearest integer (ties to
+ *     even) and saturated to [-127, 127], both in fp32; a NaN quotient codes
+ *     to 0; pruning again acts on the codes.
  */
 #include <math.h>
 #include <stdint.h>
@@ -355,6 +359,52 @@ int oracle_quantize_e4m3_rows(int dt, int64_t rows, int64_t K, const void *src, 
             float t = v / sc;
             q[r * K + k] = oracle_encode_e4m3((double)t);
         }
+    }
+    return OR_OK;
+}
+
+/* The int8 code of an fp32 quotient: round to the nearest integer, ties to
+ * even (the C default rounding mode of nearbyintf), then saturate to
+ * [-127, 127], the symmetric int8 range; a NaN quotient (only from an
+ * infinite scale meeting an infinite element) codes to 0. */
+int8_t oracle_encode_i8(float t)
+{
+    if (isnan(t))
+        return 0;
+    float r = nearbyintf(t);
+    if (r > 127.0f)
+        r = 127.0f;
+    if (r < -127.0f)
+        r = -127.0f;
+    return (int8_t)r;
+}
+
+/* The same per-row quantization to symmetric int8 (the 2:4-versus-
+ * quantization paper, section 2 "Quantization": one scale per row, and 4.2
+ * "Speed": 2:4 with INT8): s = max|x| / 127 (s = 1 for an all-zero row), q =
+ * int8(x / s), the scale and the quotients in fp32 as above; a NaN does not
+ * count toward the maximum. */
+int oracle_quantize_i8_rows(int dt, int64_t rows, int64_t K, const void *src, int64_t ld_src,
+                            int8_t *q, float *scales)
+{
+    if (dt != OR_F16 && dt != OR_BF16)
+        return OR_E_ARG;
+    if (rows < 0 || K < 0 || ld_src < K)
+        return OR_E_ARG;
+    int eb = elem_bytes(dt);
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const char *row = (const char *)src + (size_t)(r * ld_src) * eb;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf((float)decode_elem(dt, row, k));
+            if (a > amax)
+                amax = a;
+        }
+        float sc = amax > 0.0f ? amax / 127.0f : 1.0f;
+        scales[r] = sc;
+        for (int64_t k = 0; k < K; ++k)
+            q[r * K + k] = oracle_encode_i8((float)decode_elem(dt, row, k) / sc);
     }
     return OR_OK;
 }

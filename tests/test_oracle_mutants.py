@@ -13,6 +13,7 @@ from tests import test_oracle_gemm as gemm
 from tests import test_oracle_int8 as int8
 from tests import test_oracle_prune as prune
 from tests import test_oracle_quant as quant
+from tests import test_oracle_quant_i8 as quant_i8
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "sp24_oracle.c")
 
@@ -42,6 +43,15 @@ MUTANTS = [
     ("audit-ignores-eligibility", "if (eligible[i] && sparse[i]) {", "if (sparse[i]) {"),
     ("int8-magnitude-from-bits", "    if (dt == OR_I8) {\n        int v", "    if (0) {\n        int v"),
     ("int8-decoded-unsigned", "return (double)((const int8_t *)base)[i];", "return (double)((const uint8_t *)base)[i];"),
+    ("i8-scale-off", "amax / 127.0f", "amax / 128.0f"),
+    ("i8-zero-row-scale", "amax / 127.0f : 1.0f", "amax / 127.0f : 0.0f"),
+    ("i8-ties-away", "float r = nearbyintf(t);", "float r = roundf(t);"),
+    ("i8-negative-saturation", "if (r < -127.0f)\n        r = -127.0f;", "if (r < -128.0f)\n        r = -128.0f;"),
+    ("i8-nan-to-max", "if (isnan(t))\n        return 0;", "if (isnan(t))\n        return 127;"),
+    ("i8-code-decided-in-fp64", "oracle_encode_i8((float)decode_elem(dt, row, k) / sc)",
+     "oracle_encode_i8((float)rint(decode_elem(dt, row, k) / (double)sc))"),
+    ("i8-nan-counts-in-max", "            if (a > amax)\n                amax = a;\n        }\n        float sc = amax > 0.0f ? amax / 127.0f",
+     "            if (!(a <= amax))\n                amax = a;\n        }\n        float sc = amax > 0.0f ? amax / 127.0f"),
 ]
 
 PINS = [
@@ -68,6 +78,11 @@ PINS = [
     int8.test_decode_every_int8_pattern,
     int8.test_prune_matches_brute_force_and_orders_minus_128_first,
     int8.test_int8_gemm_is_exact_integer_arithmetic,
+    quant_i8.test_encode_i8_hand_picked,
+    lambda: quant_i8.test_quantize_i8_exact_multiples(oracle.BF16),
+    lambda: quant_i8.test_quantize_i8_maximum_bound_symmetry_monotone(oracle.F16),
+    quant_i8.test_quantize_i8_zero_row_nan_and_inf,
+    quant_i8.test_quantize_i8_decides_codes_in_fp32,
 ]
 
 
