@@ -31,7 +31,7 @@ printed.
 --counter-pass runs each chain eagerly (no HIP graph) with at most a few
 launches per chain, for rocprofv3 counter collection.
 
-Workloads: tiny | decode | prefill | fp8 | int8 | online | online_fp8 | hybrid | ksplit
+Workloads: tiny | decode | prefill | fp8 | int8 | online | online_fp8 | online_int8 | hybrid | ksplit
 """
 from __future__ import annotations
 
@@ -130,7 +130,23 @@ def traffic_per_launch(kernel, workload):
 # every launch reads its weights from HBM -- as the layers of a decode step do.  Warm kernels re-run
 # on one copy.
 COLD_BYTES = 640 << 20
-ONLINE = ("online", "online_fp8")   # the activation is the compressed operand, compressed every call
+ONLINE = ("online", "online_fp8", "online_int8")   # the activation is the compressed operand, compressed every call
+# the activation arrives in bf16 and each side quantizes it itself: fused with the prune for the sparse
+# side, plain for the dense side
+QUANT_ONLINE = ("online_fp8", "online_int8")
+
+
+def quantizers(workload):
+    """(fused quantize + prune + compress, plain quantize) of a quantized online workload."""
+    if workload == "online_int8":
+        return sp.quantize_i8_prune_compress, sp.quantize_i8
+    return sp.quantize_prune_compress, sp.quantize_e4m3
+
+
+def oracle_quantizer(workload):
+    """The oracle's fused quantize + prune + compress of a quantized online workload."""
+    import oracle
+    return oracle.quantize_i8_prune_compress if workload == "online_int8" else oracle.quantize_prune_compress
 HYBRID = "hybrid"                   # weight rows split: 2:4 rows and dense rows in one launch
 KSPLIT = "ksplit"                   # weight K range split: a 2:4 range and a dense range, one launch
 MAX_COPIES = 64
@@ -209,7 +225,7 @@ def build_cases(workload, cold):
             if workload == HYBRID:
                 item["Ys"] = torch.empty((M, shape["NS"]), dtype=ytype, device="cuda")
                 item["Ydd"] = torch.empty((M, shape["ND"]), dtype=ytype, device="cuda")
-            if workload == "online_fp8":
+            if workload in QUANT_ONLINE:
                 # each side quantizes the bf16 activation itself: fused with the prune for the
                 # sparse side, plain for the dense side
                 item["xs"] = torch.empty(M, dtype=torch.float32, device="cuda")
@@ -243,17 +259,18 @@ def chains(workload, cases):
                         lambda i, pick=pick, Kc=Kc: sp.decompress(pick(i)["v"], pick(i)["m"], Kc, out=pick(i)["Wp"])))
         for it in c["ms"]:
             M, key = it["M"], (c["s"], it["j"])
-            if workload == "online_fp8":
+            if workload in QUANT_ONLINE:
                 W, sw = cp[0]["W"], c["sw"]
+                fused, plain = quantizers(workload)
                 out.append((("compress",) + key, Lc,
-                            lambda i, it=it: sp.quantize_prune_compress(it["X"], values=it["xv"], meta=it["xm"],
-                                                                        scales=it["xs"])))
+                            lambda i, it=it, fused=fused: fused(it["X"], values=it["xv"], meta=it["xm"],
+                                                                scales=it["xs"])))
                 out.append((("sparse",) + key, Lg,
                             lambda i, it=it, W=W, sw=sw, M=M, N=N, K=K:
                             sp.sp24_gemm(sp.SPARSE_X, it["xv"], it["xm"], W, M, N, K, scale_x=it["xs"],
                                          scale_w=sw, out=it["Y"])))
                 out.append((("prep",) + key, Lc,
-                            lambda i, it=it: sp.quantize_e4m3(it["X"], out=it["xq"], scales=it["xqs"])))
+                            lambda i, it=it, plain=plain: plain(it["X"], out=it["xq"], scales=it["xqs"])))
                 out.append((("dense",) + key, Lg,
                             lambda i, it=it, W=W, sw=sw: sp.dense_gemm(it["xq"], W, scale_x=it["xqs"], scale_w=sw,
                                                                        out=it["Yd"])))
@@ -420,7 +437,8 @@ def compressed_operands(workload):
 
 
 def cpu_compress(workload, budget_s):
-    """The oracle's prune+compress (the fused quantize + prune + compress for online_fp8) on the full
+    """The oracle's prune+compress (the fused quantize + prune + compress for the quantized online
+    workloads) on the full
     operands of the workload, with every OpenMP thread and with one, in GB/s of algorithmic bytes."""
     import oracle
 
@@ -432,8 +450,8 @@ def cpu_compress(workload, budget_s):
         for name, dt, bits in compressed_operands(workload):
             R, K = bits.shape
             t0 = time.perf_counter()
-            if workload == "online_fp8":
-                oracle.quantize_prune_compress(dt, bits)
+            if workload in QUANT_ONLINE:
+                oracle_quantizer(workload)(dt, bits)
                 nbytes += R * K * 2 + R * K // 2 + R * K // 8 + 4 * R
             else:
                 oracle.prune_compress(dt, bits)
@@ -478,8 +496,8 @@ def cpu_baseline(workload, budget_s):
             xv = xm = None
             if workload == "online":
                 xv, xm = oracle.prune_compress(dt, xb)
-            elif workload == "online_fp8":
-                xv, xm, sx = oracle.quantize_prune_compress(w["act"], xb)
+            elif workload in QUANT_ONLINE:
+                xv, xm, sx = oracle_quantizer(workload)(w["act"], xb)
             prepared.append((N, K, M, rows, mrows, wb, sw, wv, wm, xb, sx, xv, xm))
     flops = 0.0
     secs = 0.0
@@ -632,13 +650,13 @@ def measure(workload, args, steps, warmup, cpu_budget, eager=False):
                 row.update(K_s=c["KS"], K_d=c["KD"])
             if workload in ONLINE:
                 tc = float(np.median(times[("compress",) + key]))
-                tp = float(np.median(times[("prep",) + key])) if workload == "online_fp8" else 0.0
+                tp = float(np.median(times[("prep",) + key])) if workload in QUANT_ONLINE else 0.0
                 row["t_compress_us"] = round(tc, 2)
-                if workload == "online_fp8":
+                if workload in QUANT_ONLINE:
                     row["t_dense_quantize_us"] = round(tp, 2)
                 row["speedup_incl_compress"] = round((tp + tdm) / (tc + tsm), 3)
                 tot["compress_t"] += sum(times[("compress",) + key])
-                cb = (M * K * 2 + M * K // 2 + M * K // 8 + 4 * M) if workload == "online_fp8" \
+                cb = (M * K * 2 + M * K // 2 + M * K // 8 + 4 * M) if workload in QUANT_ONLINE \
                     else compress_bytes(M, K, eb)
                 tot["compress_bytes"] += cb * len(times[("compress",) + key])
             rows.append(row)
@@ -722,7 +740,7 @@ def measure(workload, args, steps, warmup, cpu_budget, eager=False):
         for c in cases:
             for it in c["ms"]:
                 M, N, K = it["M"], c["N"], c["K"]
-                if workload == "online_fp8":
+                if workload in QUANT_ONLINE:
                     # both sides quantize; the tactic compares the rest: prune+compress of the codes
                     # and the sparse GEMM against the dense GEMM on the codes
                     rec = sp.select_tactic(sp.SPARSE_X, it["xv"], it["xm"], c["copies"][0]["W"], it["xq"], M, N, K,
@@ -807,7 +825,8 @@ def compact(rec):
     return out
 
 
-ORDER = [n for n in ("prefill", "tiny", "decode", "fp8", "int8", "online", "online_fp8", "hybrid", "ksplit")
+ORDER = [n for n in ("prefill", "tiny", "decode", "fp8", "int8", "online", "online_fp8", "online_int8", "hybrid",
+                    "ksplit")
          if n in inputs.WORKLOADS]
 
 

@@ -159,6 +159,38 @@ sp24_status sp24_quantize_e4m3(sp24_dtype src_dt, int64_t rows, int64_t K,
                                hipStream_t stream);
 
 /*
+ * The fused online int8 path: the same one-pass quantize, prune and compress
+ * with symmetric int8 codes (the 2:4-versus-quantization paper, section 4.2
+ * "Speed": 2:4 with INT8; section 2 "Quantization": one scale per row).
+ * Per row r of the f16 / bf16 source:
+ *   scales[r] = max|x| / 127 in fp32 (1 for an all-zero row; a NaN does not
+ *               count toward the maximum);
+ *   codes     = x / scales[r] in fp32 (correctly rounded), rounded to the
+ *               nearest integer (ties to even) and saturated to [-127, 127];
+ *               a NaN quotient codes to 0, so -128 never occurs;
+ *   then the magnitude 2:4 prune and compress of the codes, exactly as
+ *   sp24_prune_compress does for SP24_I8 input.
+ *   Dtypes, sizes, strides, alignment and errors as sp24_quantize_prune_compress;
+ *   values out: rows x K/2 int8;  meta out: rows x K/32 words;  scales out: rows
+ *   fp32.  The outputs feed sp24_gemm(SP24_SPARSE_X, SP24_I8, ..., scale_x =
+ *   scales, ...).
+ */
+sp24_status sp24_quantize_i8_prune_compress(sp24_dtype src_dt, int64_t rows, int64_t K,
+                                            const void *src, int64_t ld_src,
+                                            void *values, uint32_t *meta, float *scales,
+                                            hipStream_t stream);
+
+/*
+ * The same per-row int8 quantization without the prune: every code, rows x K
+ * int8 into `dst` (row stride K), one fp32 scale per row -- the dense int8
+ * GEMM's input on the online int8 comparison.  Same dtypes, sizes, alignment
+ * and errors as above.
+ */
+sp24_status sp24_quantize_i8(sp24_dtype src_dt, int64_t rows, int64_t K,
+                             const void *src, int64_t ld_src, void *dst, float *scales,
+                             hipStream_t stream);
+
+/*
  * Sparse x dense GEMM, Y = X * W^T (the paper's section 2 "Sparse tensor
  * cores": the compressed first operand and its indices select the matching
  * elements of the dense operand).

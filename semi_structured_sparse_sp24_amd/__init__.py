@@ -15,6 +15,8 @@ PyTorch fallback: if the library is missing, every call raises.
   gemm_kernel(...)             -> name of the kernel a GEMM call would launch (host only)
   quantize_prune_compress(x)   -> (values e4m3, meta, scales): fused online fp8 path
   quantize_e4m3(x)             -> (codes e4m3, scales): the dense side's quantization
+  quantize_i8_prune_compress(x) -> (values int8, meta, scales): fused online int8 path
+  quantize_i8(x)               -> (codes int8, scales): its dense side
   hybrid_gemm(...)             -> Y = X [Ws | Wd]^T, Ws compressed and Wd dense rows, one launch
   ksplit_gemm(...)             -> Y = X W^T, W's first K_s columns compressed and the rest dense, one launch
   audit_aggregate(...)         -> layer counts, ratios and Sparse GPU-Time Coverage (host only)
@@ -83,6 +85,8 @@ SIGNATURES = {
                                     ctypes.POINTER(AuditMetrics)]),
     "sp24_quantize_prune_compress": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp]),
     "sp24_quantize_e4m3": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "sp24_quantize_i8_prune_compress": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp]),
+    "sp24_quantize_i8": (_i32, [_i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -218,47 +222,65 @@ def prune_compress(dense: torch.Tensor, values=None, meta=None):
     return values, meta
 
 
-def quantize_prune_compress(x: torch.Tensor, values=None, meta=None, scales=None):
-    """Per-row e4m3 quantization fused with the 2:4 prune and compress:
-    (values rows x K/2 e4m3, meta rows x K/32 int32, scales rows fp32)."""
+def _quantize_pruned(fn, code_dtype, x, values, meta, scales):
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
-        raise ValueError("quantize_prune_compress takes a 2-D tensor")
+        raise ValueError(f"{fn} takes a 2-D tensor")
     rows, K = x.shape
     _mat(x, "x", rows, K, ld_min=K)
     if values is None:
-        values = torch.empty((rows, K // 2), dtype=torch.float8_e4m3fn, device=x.device)
+        values = torch.empty((rows, K // 2), dtype=code_dtype, device=x.device)
     if meta is None:
         meta = torch.empty((rows, (K + 31) // 32), dtype=torch.int32, device=x.device)
     if scales is None:
         scales = torch.empty(rows, dtype=torch.float32, device=x.device)
-    _compressed(values, meta, rows, K, torch.float8_e4m3fn, "output")
+    _compressed(values, meta, rows, K, code_dtype, "output")
     _vec(scales, "scales", rows)
     _same_device(x, values, meta, scales)
     ld = x.stride(0) if rows > 1 else K
-    st = lib().sp24_quantize_prune_compress(_code(x), rows, K, _ptr(x), ld, _ptr(values), _ptr(meta),
-                                            _ptr(scales), _stream(x.device))
-    _check("sp24_quantize_prune_compress", st)
+    st = getattr(lib(), "sp24_" + fn)(_code(x), rows, K, _ptr(x), ld, _ptr(values), _ptr(meta), _ptr(scales),
+                                      _stream(x.device))
+    _check("sp24_" + fn, st)
     return values, meta, scales
+
+
+def _quantize_codes(fn, code_dtype, x, out, scales):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{fn} takes a 2-D tensor")
+    rows, K = x.shape
+    _mat(x, "x", rows, K, ld_min=K)
+    if out is None:
+        out = torch.empty((rows, K), dtype=code_dtype, device=x.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _mat(out, "out", rows, K, code_dtype)
+    _vec(scales, "scales", rows)
+    _same_device(x, out, scales)
+    ld = x.stride(0) if rows > 1 else K
+    st = getattr(lib(), "sp24_" + fn)(_code(x), rows, K, _ptr(x), ld, _ptr(out), _ptr(scales), _stream(x.device))
+    _check("sp24_" + fn, st)
+    return out, scales
+
+
+def quantize_prune_compress(x: torch.Tensor, values=None, meta=None, scales=None):
+    """Per-row e4m3 quantization fused with the 2:4 prune and compress:
+    (values rows x K/2 e4m3, meta rows x K/32 int32, scales rows fp32)."""
+    return _quantize_pruned("quantize_prune_compress", torch.float8_e4m3fn, x, values, meta, scales)
 
 
 def quantize_e4m3(x: torch.Tensor, out=None, scales=None):
     """Per-row e4m3 quantization: (codes rows x K e4m3, scales rows fp32)."""
-    if not isinstance(x, torch.Tensor) or x.dim() != 2:
-        raise ValueError("quantize_e4m3 takes a 2-D tensor")
-    rows, K = x.shape
-    _mat(x, "x", rows, K, ld_min=K)
-    if out is None:
-        out = torch.empty((rows, K), dtype=torch.float8_e4m3fn, device=x.device)
-    if scales is None:
-        scales = torch.empty(rows, dtype=torch.float32, device=x.device)
-    _mat(out, "out", rows, K, torch.float8_e4m3fn)
-    _vec(scales, "scales", rows)
-    _same_device(x, out, scales)
-    ld = x.stride(0) if rows > 1 else K
-    st = lib().sp24_quantize_e4m3(_code(x), rows, K, _ptr(x), ld, _ptr(out), _ptr(scales),
-                                  _stream(x.device))
-    _check("sp24_quantize_e4m3", st)
-    return out, scales
+    return _quantize_codes("quantize_e4m3", torch.float8_e4m3fn, x, out, scales)
+
+
+def quantize_i8_prune_compress(x: torch.Tensor, values=None, meta=None, scales=None):
+    """Per-row symmetric int8 quantization fused with the 2:4 prune and
+    compress: (values rows x K/2 int8, meta rows x K/32 int32, scales rows fp32)."""
+    return _quantize_pruned("quantize_i8_prune_compress", torch.int8, x, values, meta, scales)
+
+
+def quantize_i8(x: torch.Tensor, out=None, scales=None):
+    """Per-row symmetric int8 quantization: (codes rows x K int8, scales rows fp32)."""
+    return _quantize_codes("quantize_i8", torch.int8, x, out, scales)
 
 
 def decompress(values: torch.Tensor, meta: torch.Tensor, K: int, out=None):

@@ -167,8 +167,9 @@ SP24_API sp24_status sp24_decompress(sp24_dtype dt, int64_t rows, int64_t K, con
 // one 256-lane workgroup per row: the grid stays below 2^32 lanes
 static constexpr int64_t kMaxQuantRows = (int64_t)1 << 24;
 
-static sp24_status quantize_impl(const sp24_dtype& dt, int64_t rows, int64_t K, const void* src, int64_t ld_src,
-                                 void* out, uint32_t* meta, float* scales, bool prune, hipStream_t stream) {
+static sp24_status quantize_impl(const sp24_dtype& dt, sp24_dtype out_dt, int64_t rows, int64_t K,
+                                 const void* src, int64_t ld_src, void* out, uint32_t* meta, float* scales,
+                                 bool prune, hipStream_t stream) {
     if (!dtype_known(enum_bits(dt)) || (dt != SP24_F16 && dt != SP24_BF16))
         return SP24_E_DTYPE;
     if (rows < 0 || K < 0 || ld_src < K || rows > kMaxQuantRows)
@@ -180,19 +181,31 @@ static sp24_status quantize_impl(const sp24_dtype& dt, int64_t rows, int64_t K, 
     if (K % 32 != 0 || ld_src % 8 != 0 || !aligned16(src) || !aligned16(out) || (prune && !aligned16(meta)) ||
         ((uintptr_t)scales & 3u))
         return SP24_E_ALIGN;
-    return launch_quantize_e4m3(dt, rows, K, src, ld_src, out, prune ? meta : nullptr, scales, stream) == hipSuccess
+    return launch_quantize(dt, out_dt, rows, K, src, ld_src, out, prune ? meta : nullptr, scales, stream) ==
+                   hipSuccess
                ? SP24_OK : SP24_E_HIP;
 }
 
 SP24_API sp24_status sp24_quantize_prune_compress(sp24_dtype src_dt, int64_t rows, int64_t K, const void* src,
                                                   int64_t ld_src, void* values, uint32_t* meta, float* scales,
                                                   hipStream_t stream) {
-    return quantize_impl(src_dt, rows, K, src, ld_src, values, meta, scales, true, stream);
+    return quantize_impl(src_dt, SP24_E4M3, rows, K, src, ld_src, values, meta, scales, true, stream);
 }
 
 SP24_API sp24_status sp24_quantize_e4m3(sp24_dtype src_dt, int64_t rows, int64_t K, const void* src,
                                         int64_t ld_src, void* dst, float* scales, hipStream_t stream) {
-    return quantize_impl(src_dt, rows, K, src, ld_src, dst, nullptr, scales, false, stream);
+    return quantize_impl(src_dt, SP24_E4M3, rows, K, src, ld_src, dst, nullptr, scales, false, stream);
+}
+
+SP24_API sp24_status sp24_quantize_i8_prune_compress(sp24_dtype src_dt, int64_t rows, int64_t K, const void* src,
+                                                     int64_t ld_src, void* values, uint32_t* meta, float* scales,
+                                                     hipStream_t stream) {
+    return quantize_impl(src_dt, SP24_I8, rows, K, src, ld_src, values, meta, scales, true, stream);
+}
+
+SP24_API sp24_status sp24_quantize_i8(sp24_dtype src_dt, int64_t rows, int64_t K, const void* src,
+                                      int64_t ld_src, void* dst, float* scales, hipStream_t stream) {
+    return quantize_impl(src_dt, SP24_I8, rows, K, src, ld_src, dst, nullptr, scales, false, stream);
 }
 
 static sp24_status gemm_impl(const sp24_operand& which, const sp24_dtype& in_dt, const sp24_dtype& out_dt, int64_t M,

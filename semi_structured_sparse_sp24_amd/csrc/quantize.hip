@@ -1,17 +1,22 @@
-// quantize.hip -- per-row fp8 (e4m3) quantization of a 16-bit operand, fused
-// with the magnitude 2:4 prune and compress for dynamic activations.
+// quantize.hip -- per-row quantization of a 16-bit operand to fp8 (e4m3) or
+// int8, fused with the magnitude 2:4 prune and compress for dynamic
+// activations.
 //
 // The online path of the 2:4-versus-quantization paper (section 3.5, "Measuring
-// speed", and 4.2, "Speed"): the activation is quantized, pruned and compressed
-// in one pass that reads it once and writes the kept values and their indices
-// once; one scale per row (section 2, "Quantization").  Per row:
-//   s = max|x| / 448   (1 for an all-zero row; a NaN does not count), in fp32;
-//   q = e4m3(x / s)    x / s in fp32 (correctly rounded division), then round
-//                      to nearest even to OCP e4m3fn, saturating at 448;
+// speed", and 4.2, "Speed", which lists 2:4 with FP8 and with INT8): the
+// activation is quantized, pruned and compressed in one pass that reads it
+// once and writes the kept values and their indices once; one scale per row
+// (section 2, "Quantization").  Per row, with Q = 448 (e4m3) or 127 (int8):
+//   s = max|x| / Q     (1 for an all-zero row; a NaN does not count), in fp32;
+//   q = code(x / s)    x / s in fp32 (correctly rounded division), then
+//                      e4m3: round to nearest even to OCP e4m3fn, saturating
+//                            at 448;
+//                      int8: round to the nearest integer, ties to even,
+//                            saturated to [-127, 127]; a NaN codes to 0;
 //   prune: in every group of four codes keep the two of largest magnitude
 //   (ties to the lower index) -- the codes are what the GEMM consumes, so the
 //   selection is made on them.
-// The plain variant writes all codes (the dense fp8 GEMM's input).
+// The plain variant writes all codes (the dense GEMM's input).
 //
 // A workgroup of 256 lanes per row.  Lane t takes the 16-element chunks
 // t, t + 256, ... (two 16-byte loads each) and keeps them in registers: the
@@ -22,13 +27,19 @@
 // Codes without the division.  With y = 1/s (correctly rounded, once per row,
 // then lowered by 2^-21 relative) t = x * y lies below x / s in magnitude, by
 // 5 to 11 units of 2^-24 relative; so the fp32 quotient q lies strictly above
-// t and at most 23 fp32 ulps of t beyond it, and |t| < 448.  Rounding is
-// monotone: when t and the fp32 value 32 ulps beyond it (its bit pattern + 32)
-// convert to the same e4m3 code, so does every value between them, q
-// included, and the hardware conversion of t is the code.  Otherwise (about
-// one element in 3 * 10^4 for Gaussian rows) the four elements of that word
-// take the exact division and the bitwise encoder, as do rows holding an
-// infinity or a NaN, or whose scale is below the fp32 normals.
+// t and at most 23 fp32 ulps of t beyond it, and |t| < Q.
+//   e4m3: rounding is monotone, so when t and the fp32 value 32 ulps beyond
+//   it (its bit pattern + 32) convert to the same code, so does every value
+//   between them, q included, and the hardware conversion of t is the code.
+//   int8: |q - t| < 2^-13 (|q| <= 128), so when t lies more than 2^-12 from
+//   the nearest half-integer, q rounds to the same integer as t.
+// Otherwise the four elements of that word take the correctly rounded
+// division, whose quotients (at most an ulp beyond Q) the same conversions
+// then code exactly.  Such near-ties are not rare: a 16-bit x over a 16-bit maximum
+// often lands exactly on an e4m3 midpoint (about one element in 200 of a
+// Gaussian bf16 row in e4m3, one in 2500 in int8).  Rows holding an infinity
+// or a NaN, or whose scale is below the fp32 normals, take the division and a
+// bitwise encoder for every element.
 #include "sp24_internal.h"
 
 namespace sp24 {
@@ -116,6 +127,77 @@ __device__ __forceinline__ void top2_pair(uint32_t A, uint32_t B, uint32_t& lo, 
     hi = pmax(pa, pb);
 }
 
+// The two code formats.  fast4: the codes of four values t = x * y (element
+// order from the low byte) and whether any of them must be redone exactly;
+// convert4: the codes of four quotients of a finite row (within an ulp of
+// the code range, where the fast conversion is exact); exact: the code of any
+// fp32 quotient (non-finite and saturating ones included); mag: per byte, the
+// magnitude the 2:4 selection ranks (top2_pair reads its low seven bits).
+template <sp24_dtype OUT>
+struct Codec;
+
+template <>
+struct Codec<SP24_E4M3> {
+    static constexpr float kQ = 448.0f;
+    static __device__ __forceinline__ uint32_t fast4(const float (&t)[4], bool& redo) {
+        const uint32_t q = cvt4(t[0], t[1], t[2], t[3]);
+        redo = q != cvt4(above(t[0]), above(t[1]), above(t[2]), above(t[3]));
+        return q;
+    }
+    // a finite row's quotient can exceed 448 by an ulp (s rounded down), where the clamp gives the
+    // code that rounding with saturation gives
+    static __device__ __forceinline__ uint32_t convert4(const float (&q)[4]) {
+        float c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            c[j] = __builtin_fminf(__builtin_fmaxf(q[j], -448.0f), 448.0f);
+        return cvt4(c[0], c[1], c[2], c[3]);
+    }
+    static __device__ __forceinline__ uint32_t exact(float v) { return e4m3_rne_sat(v); }
+    static __device__ __forceinline__ uint32_t mag(uint32_t w) { return w; }   // sign-magnitude bytes
+};
+
+template <>
+struct Codec<SP24_I8> {
+    static constexpr float kQ = 127.0f;
+    // adding 1.5 * 2^23 rounds to an integer, ties to even, and leaves it
+    // (two's complement, |v| < 2^22) in the low mantissa bits
+    static __device__ __forceinline__ uint32_t pack4(const uint32_t (&b)[4]) {
+        return __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                     __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+    }
+    static __device__ __forceinline__ uint32_t fast4(const float (&t)[4], bool& redo) {
+        uint32_t b[4];
+        bool r = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float m = t[j] + 0x1.8p23f;
+            r = r || __builtin_fabsf(t[j] - (m - 0x1.8p23f)) > 0.5f - 0x1p-12f;
+            b[j] = __builtin_bit_cast(uint32_t, m);
+        }
+        redo = r;
+        return pack4(b);
+    }
+    static __device__ __forceinline__ uint32_t convert4(const float (&q)[4]) {
+        uint32_t b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            b[j] = __builtin_bit_cast(uint32_t, q[j] + 0x1.8p23f);
+        return pack4(b);
+    }
+    static __device__ __forceinline__ uint32_t exact(float v) {
+        if (__builtin_isnan(v))
+            return 0u;
+        const float r = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v), -127.0f), 127.0f);
+        return (uint32_t)(int)r & 0xffu;
+    }
+    // |q| per byte: codes are never -128, so (q ^ 0xff) + 1 stays within the byte
+    static __device__ __forceinline__ uint32_t mag(uint32_t w) {
+        const uint32_t sg = (w >> 7) & 0x01010101u;
+        return (w ^ (sg * 0xffu)) + sg;
+    }
+};
+
 // Maximum over the 64 lanes, in every lane: a prefix maximum within each row
 // of 16 lanes (DPP row shifts, the lanes shifted in from outside the row read
 // 0), the row results carried across rows by the row broadcasts, then lane 63.
@@ -141,7 +223,7 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v, uint32_t* red) {
 
 // One row per workgroup, CH chunks per lane and round.  PRUNE: write kept
 // codes + metadata; else write every code.
-template <sp24_dtype DT, bool PRUNE, int CH>
+template <sp24_dtype DT, sp24_dtype OUT, bool PRUNE, int CH>
 __global__ void __launch_bounds__(kThreads)
 quantize_rows(const uint8_t* __restrict__ src, int64_t ld_bytes, int64_t K,
               uint8_t* __restrict__ out, uint8_t* __restrict__ meta, float* __restrict__ scales) {
@@ -198,7 +280,7 @@ quantize_rows(const uint8_t* __restrict__ src, int64_t ld_bytes, int64_t K,
             }
             amax = row_max_u32(m, red[1]);
         }
-        const float s = amax ? __fdiv_rn(bits_to_float(amax, DT), 448.0f) : 1.0f;
+        const float s = amax ? __fdiv_rn(bits_to_float(amax, DT), Codec<OUT>::kQ) : 1.0f;
         const float y = __fdiv_rn(1.0f, s) * (1.0f - 0x1p-21f);
         const bool exact_row = amax_raw >= kInf || !(s >= 0x1p-126f);
         if (lr == 0)
@@ -221,7 +303,7 @@ quantize_rows(const uint8_t* __restrict__ src, int64_t ld_bytes, int64_t K,
                     x[2 * i + 1] = bits_to_float(w[i] >> 16, DT);
                 }
                 uint32_t qw[4];                 // four codes per word, element order
-                bool any = exact_row;
+                bool any = false;
                 bool redo[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -229,19 +311,30 @@ quantize_rows(const uint8_t* __restrict__ src, int64_t ld_bytes, int64_t K,
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         t[j] = x[4 * i + j] * y;
-                    qw[i] = cvt4(t[0], t[1], t[2], t[3]);
-                    redo[i] = qw[i] != cvt4(above(t[0]), above(t[1]), above(t[2]), above(t[3]));
+                    qw[i] = Codec<OUT>::fast4(t, redo[i]);
                     any = any || redo[i];
                 }
-                if (any) {
+                if (exact_row) {
+                    // non-finite or tiny-scale rows: every code from the division and the bitwise encoder
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        if (exact_row || redo[i]) {
-                            uint32_t q = 0;
+                        uint32_t q = 0;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            q |= Codec<OUT>::exact(__fdiv_rn(x[4 * i + j], s)) << (8 * j);
+                        qw[i] = q;
+                    }
+                } else if (any) {
+                    // a finite row: the correctly rounded quotients lie within the code range, where the
+                    // fast conversion is exact
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (redo[i]) {
+                            float q[4];
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
-                                q |= e4m3_rne_sat(__fdiv_rn(x[4 * i + j], s)) << (8 * j);
-                            qw[i] = q;
+                                q[j] = __fdiv_rn(x[4 * i + j], s);
+                            qw[i] = Codec<OUT>::convert4(q);
                         }
                     }
                 }
@@ -250,7 +343,7 @@ quantize_rows(const uint8_t* __restrict__ src, int64_t ld_bytes, int64_t K,
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         uint32_t p0, p1;
-                        top2_pair(qw[2 * h], qw[2 * h + 1], p0, p1);
+                        top2_pair(Codec<OUT>::mag(qw[2 * h]), Codec<OUT>::mag(qw[2 * h + 1]), p0, p1);
                         const uint32_t n = p0 | (p1 << 2);           // a metadata nibble per half
                         nib |= ((n & 0xfu) | ((n >> 12) & 0xf0u)) << (8 * h);
                         // bytes p of qw[2h] are selector values 0..3, of qw[2h+1] 4..7
@@ -267,46 +360,49 @@ quantize_rows(const uint8_t* __restrict__ src, int64_t ld_bytes, int64_t K,
     }
 }
 
-template <sp24_dtype DT, bool PRUNE, int CH>
+template <sp24_dtype DT, sp24_dtype OUT, bool PRUNE, int CH>
 void launch_shape(int64_t rows, int64_t K, const uint8_t* src, int64_t ld_bytes, uint8_t* out, uint8_t* meta,
                   float* scales, hipStream_t s) {
-    hipLaunchKernelGGL((quantize_rows<DT, PRUNE, CH>), dim3((uint32_t)rows), dim3(kThreads), 0, s, src, ld_bytes,
-                       K, out, meta, scales);
+    hipLaunchKernelGGL((quantize_rows<DT, OUT, PRUNE, CH>), dim3((uint32_t)rows), dim3(kThreads), 0, s, src,
+                       ld_bytes, K, out, meta, scales);
 }
 
 // Chunks per lane: the whole row in registers up to K = 32768, longer rows in rounds.
-template <sp24_dtype DT, bool PRUNE>
+template <sp24_dtype DT, sp24_dtype OUT, bool PRUNE>
 hipError_t launch_dt(int64_t rows, int64_t K, const uint8_t* src, int64_t ld_bytes, uint8_t* out, uint8_t* meta,
                      float* scales, hipStream_t s) {
     const int64_t chunks = K / 16;
     if (chunks <= kThreads)
-        launch_shape<DT, PRUNE, 1>(rows, K, src, ld_bytes, out, meta, scales, s);
+        launch_shape<DT, OUT, PRUNE, 1>(rows, K, src, ld_bytes, out, meta, scales, s);
     else if (chunks <= 2 * kThreads)
-        launch_shape<DT, PRUNE, 2>(rows, K, src, ld_bytes, out, meta, scales, s);
+        launch_shape<DT, OUT, PRUNE, 2>(rows, K, src, ld_bytes, out, meta, scales, s);
     else if (chunks <= 4 * kThreads)
-        launch_shape<DT, PRUNE, 4>(rows, K, src, ld_bytes, out, meta, scales, s);
+        launch_shape<DT, OUT, PRUNE, 4>(rows, K, src, ld_bytes, out, meta, scales, s);
     else
-        launch_shape<DT, PRUNE, kMaxChunks>(rows, K, src, ld_bytes, out, meta, scales, s);
+        launch_shape<DT, OUT, PRUNE, kMaxChunks>(rows, K, src, ld_bytes, out, meta, scales, s);
     return hipGetLastError();
 }
 
-template <bool PRUNE>
+template <sp24_dtype OUT, bool PRUNE>
 hipError_t launch(sp24_dtype dt, int64_t rows, int64_t K, const void* src, int64_t ld_src, void* out,
                   uint32_t* meta, float* scales, hipStream_t s) {
     const int64_t ld_bytes = ld_src * 2;
     if (dt == SP24_BF16)
-        return launch_dt<SP24_BF16, PRUNE>(rows, K, (const uint8_t*)src, ld_bytes, (uint8_t*)out, (uint8_t*)meta,
+        return launch_dt<SP24_BF16, OUT, PRUNE>(rows, K, (const uint8_t*)src, ld_bytes, (uint8_t*)out,
+                                                (uint8_t*)meta, scales, s);
+    return launch_dt<SP24_F16, OUT, PRUNE>(rows, K, (const uint8_t*)src, ld_bytes, (uint8_t*)out, (uint8_t*)meta,
                                            scales, s);
-    return launch_dt<SP24_F16, PRUNE>(rows, K, (const uint8_t*)src, ld_bytes, (uint8_t*)out, (uint8_t*)meta,
-                                      scales, s);
 }
 
 }  // namespace
 
-hipError_t launch_quantize_e4m3(sp24_dtype dt, int64_t rows, int64_t K, const void* src, int64_t ld_src,
-                                void* out, uint32_t* meta, float* scales, hipStream_t s) {
-    return meta ? launch<true>(dt, rows, K, src, ld_src, out, meta, scales, s)
-                : launch<false>(dt, rows, K, src, ld_src, out, nullptr, scales, s);
+hipError_t launch_quantize(sp24_dtype dt, sp24_dtype out_dt, int64_t rows, int64_t K, const void* src,
+                           int64_t ld_src, void* out, uint32_t* meta, float* scales, hipStream_t s) {
+    if (out_dt == SP24_I8)
+        return meta ? launch<SP24_I8, true>(dt, rows, K, src, ld_src, out, meta, scales, s)
+                    : launch<SP24_I8, false>(dt, rows, K, src, ld_src, out, nullptr, scales, s);
+    return meta ? launch<SP24_E4M3, true>(dt, rows, K, src, ld_src, out, meta, scales, s)
+                : launch<SP24_E4M3, false>(dt, rows, K, src, ld_src, out, nullptr, scales, s);
 }
 
 }  // namespace sp24

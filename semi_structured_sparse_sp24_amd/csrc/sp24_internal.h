@@ -34,11 +34,12 @@ hipError_t launch_prune_compress(sp24_dtype dt, int64_t rows, int64_t K, const v
 hipError_t launch_decompress(sp24_dtype dt, int64_t rows, int64_t K, const void* values,
                              const uint32_t* meta, void* dst, int64_t ld_dst, hipStream_t s);
 
-// Per-row e4m3 quantization of a 16-bit operand: codes into `out` (rows x K,
-// meta == nullptr) or, fused with the 2:4 prune, kept codes into `out` (rows x
-// K/2) and metadata into `meta`; one fp32 scale per row into `scales`.
-hipError_t launch_quantize_e4m3(sp24_dtype dt, int64_t rows, int64_t K, const void* src, int64_t ld_src,
-                                void* out, uint32_t* meta, float* scales, hipStream_t s);
+// Per-row quantization of a 16-bit operand to out_dt (SP24_E4M3 or SP24_I8):
+// codes into `out` (rows x K, meta == nullptr) or, fused with the 2:4 prune,
+// kept codes into `out` (rows x K/2) and metadata into `meta`; one fp32 scale
+// per row into `scales`.
+hipError_t launch_quantize(sp24_dtype dt, sp24_dtype out_dt, int64_t rows, int64_t K, const void* src,
+                           int64_t ld_src, void* out, uint32_t* meta, float* scales, hipStream_t s);
 
 struct GemmArgs {
     sp24_dtype in_dt, out_dt;

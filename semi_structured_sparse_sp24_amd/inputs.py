@@ -23,6 +23,9 @@ Workloads, shaped like the linear layers of the pages' LLMs:
   online_fp8  the same X (bf16, outliers), quantized to e4m3 per row and
             pruned on every call by the library; W e4m3 (N, K) in
             {(4096,4096), (28672,4096)} with per-channel scales; M = 4096
+  online_int8  the same X, quantized to symmetric int8 per row and pruned on
+            every call by the library; W int8 (N, K) in {(4096,4096),
+            (28672,4096)} with per-channel scales; M = 4096
   int8      the fp8 shapes in symmetric per-row int8
   hybrid    the prefill weights, the last N/8 rows kept dense; M in {2048, 8192}
   ksplit    the prefill weights, the last K/4 columns kept dense; M in {2048, 8192}
@@ -56,6 +59,8 @@ WORKLOADS = {
     "online": dict(index=5, dtype=BF16, out=BF16, shapes=[(4096, 4096)], ms=[4096]),
     "online_fp8": dict(index=6, dtype=E4M3, act=BF16, out=BF16, shapes=[(4096, 4096), (28672, 4096)],
                        ms=[4096]),
+    "online_int8": dict(index=10, dtype=I8, act=BF16, out=BF16, shapes=[(4096, 4096), (28672, 4096)],
+                        ms=[4096]),
     # the fp8 shapes in symmetric per-row int8 (the 2:4 + INT8 variant)
     "int8": dict(index=8, dtype=I8, out=BF16,
                  shapes=[(5120, 5120), (51200, 5120), (5120, 25600)], ms=[1, 64, 4096]),
@@ -142,7 +147,7 @@ def activation(workload: str, s: int, j: int, M: int | None = None):
     if M is None:
         M = w["ms"][j]
     t = normal((M, K), 1.0, seed_of(w["index"], s, 1, j))
-    if workload in ("online", "online_fp8"):
+    if workload in ("online", "online_fp8", "online_int8"):
         t = outliers(t, 0.01, 20.0, seed_of(w["index"], s, 2, j))
     act = w.get("act", w["dtype"])
     if act == E4M3:

@@ -97,8 +97,10 @@ def test_select_tactic_validation():
              ctypes.byref(rec)) == 1
 
 
-def test_quantize_validation_precedes_hip():
-    f, g = sp.lib().sp24_quantize_prune_compress, sp.lib().sp24_quantize_e4m3
+@pytest.mark.parametrize("fused,plain", [("sp24_quantize_prune_compress", "sp24_quantize_e4m3"),
+                                         ("sp24_quantize_i8_prune_compress", "sp24_quantize_i8")])
+def test_quantize_validation_precedes_hip(fused, plain):
+    f, g = getattr(sp.lib(), fused), getattr(sp.lib(), plain)
     ok = dict(dt=sp.BF16, rows=4, K=64, src=16, ld=64, out=32, meta=48, sc=64)
 
     def q(**kw):

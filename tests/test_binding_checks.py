@@ -125,6 +125,14 @@ def test_quantizer_checks():
         sp.quantize_prune_compress(x, scales=torch.ones(M + 1))
     with pytest.raises(ValueError):
         sp.quantize_e4m3(x, out=torch.zeros((M, K // 2), dtype=E4))
+    with pytest.raises(TypeError):
+        sp.quantize_i8_prune_compress(x, values=torch.zeros((M, K // 2), dtype=E4))
+    with pytest.raises(ValueError):
+        sp.quantize_i8_prune_compress(x, meta=torch.zeros((M, K // 32 + 1), dtype=torch.int32))
+    with pytest.raises(TypeError):
+        sp.quantize_i8(x, out=torch.zeros((M, K), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        sp.quantize_i8(x.t())
 
 
 def test_hybrid_checks():

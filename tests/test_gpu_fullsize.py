@@ -5,6 +5,9 @@
     for byte against the oracle), then the scaled fp8 activation-compressed
     GEMM against both weight shapes; and the dense side, the plain quantizer
     and the dense fp8 GEMM on its codes;
+  - online_int8: the same activation through the fused int8 quantize +
+    prune + compress (byte for byte), then the int8 activation-compressed
+    GEMM against both weight shapes, and the dense side on the plain codes;
   - int8: every (shape, M) case, weight-compressed GEMM and the dense GEMM
     on the decompressed weight, with per-row scales (K up to 25600);
   - hybrid: every (shape, M) case of the row-split hybrid GEMM.
@@ -80,6 +83,46 @@ def test_online_fp8_end_to_end(s):
     e_s, e_d = oracle.relative_error(decode_out(Y[rt]), R), oracle.relative_error(decode_out(Yd[rt]), Rd)
     say("  rel err sparse", e_s, "dense", e_d)
     assert e_s <= TOL[oracle.E4M3] and e_d <= TOL[oracle.E4M3]
+    assert bool(torch.isfinite(Y.float()).all()) and bool(torch.isfinite(Yd.float()).all())
+
+
+@functools.lru_cache(maxsize=1)
+def _online_int8_x(s):
+    xb, _ = inputs.activation("online_int8", s, 0)
+    xv, xm, xs = oracle.quantize_i8_prune_compress(oracle.BF16, xb)
+    xq, xqs = oracle.quantize_i8_rows(oracle.BF16, xb)
+    return xb, xv, xm, xs, xq, xqs
+
+
+@pytest.mark.parametrize("s", range(len(inputs.WORKLOADS["online_int8"]["shapes"])))
+def test_online_int8_end_to_end(s):
+    w = inputs.WORKLOADS["online_int8"]
+    N, K = w["shapes"][s]
+    M = w["ms"][0]
+    name = sp.gemm_kernel(True, sp.SPARSE_X, torch.int8, torch.bfloat16, M, N, K)
+    say("full online_int8", (N, K), "M", M, name)
+    xb, xv, xm, xs, xq, xqs = _online_int8_x(s)
+    wb, sw = _weight("online_int8", s)
+    X = to_dev(xb, oracle.BF16)
+    W = to_dev(wb, oracle.I8)
+    gv, gm, gs = sp.quantize_i8_prune_compress(X)
+    gq, gqs = sp.quantize_i8(X)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(gv, oracle.I8), xv)
+    assert np.array_equal(meta_host(gm), xm)
+    assert np.array_equal(gs.cpu().numpy(), xs)
+    assert np.array_equal(to_host(gq, oracle.I8), xq)
+    assert np.array_equal(gqs.cpu().numpy(), xqs)
+    Y = sp.sp24_gemm(sp.SPARSE_X, gv, gm, W, M, N, K, scale_x=gs, scale_w=_f32(sw))
+    Yd = sp.dense_gemm(gq, W, scale_x=gqs, scale_w=_f32(sw))
+    torch.cuda.synchronize()
+    rows = band_rows(M, seed=s + 7)
+    R = oracle.gemm(oracle.I8, M, N, K, x_vals=xv, x_meta=xm, w=wb, scale_x=xs, scale_w=sw, mrows=rows)
+    Rd = oracle.gemm(oracle.I8, M, N, K, x=xq, w=wb, scale_x=xqs, scale_w=sw, mrows=rows)
+    rt = torch.from_numpy(rows).cuda()
+    e_s, e_d = oracle.relative_error(decode_out(Y[rt]), R), oracle.relative_error(decode_out(Yd[rt]), Rd)
+    say("  rel err sparse", e_s, "dense", e_d)
+    assert e_s <= TOL[oracle.I8] and e_d <= TOL[oracle.I8]
     assert bool(torch.isfinite(Y.float()).all()) and bool(torch.isfinite(Yd.float()).all())
 
 

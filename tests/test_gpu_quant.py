@@ -56,9 +56,8 @@ def test_plain_matches_oracle_bytewise(dt, rows, K):
     assert np.array_equal(_host(gq), q)
 
 
-# more rows than the workgroups resident at once (with up to 8, 6, 4, 2 of them
-# per compute unit for 1, 2, 4, 8 chunks a lane), so each workgroup walks
-# several rows with the next row's loads in flight; the last shape takes two
+# more rows than the workgroups resident at once (one row per workgroup), so
+# the rows are taken in several waves of workgroups; the last shape takes two
 # rounds per row
 LOOP_SHAPES = [(5000, 64), (1600, 4128), (1100, 8224), (600, 16416), (520, 32800)]
 
