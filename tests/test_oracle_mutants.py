@@ -83,6 +83,7 @@ PINS = [
     lambda: quant_i8.test_quantize_i8_maximum_bound_symmetry_monotone(oracle.F16),
     quant_i8.test_quantize_i8_zero_row_nan_and_inf,
     quant_i8.test_quantize_i8_decides_codes_in_fp32,
+    lambda: quant_i8.test_quantize_i8_matches_torch_fp32(oracle.BF16),
 ]
 
 

@@ -13,7 +13,9 @@ something the definition fixes independently of how the oracle computes it:
   - the quotient is formed in fp32 (elements whose fp32 and exact quotients
     round apart follow fp32);
   - the fused form keeps, in every group, the two codes of largest
-    magnitude."""
+    magnitude;
+  - an independent implementation of the same reading (torch in fp32)
+    agrees on every code and scale."""
 import numpy as np
 import pytest
 
@@ -145,3 +147,20 @@ def test_quantize_i8_prune_compress_keeps_the_largest_codes():
     assert np.array_equal(np.sort(da, axis=2)[:, :, 2:], np.sort(qa, axis=2)[:, :, 2:])
     # and the kept codes are codes of the row at their positions
     assert np.all((_i8(dense) == 0) | (_i8(dense) == _i8(q)))
+
+
+@pytest.mark.parametrize("dt", [oracle.BF16, oracle.F16])
+def test_quantize_i8_matches_torch_fp32(dt):
+    """An independent implementation of the same reading: torch's fp32 maximum,
+    division by 127 and by the scale (IEEE, correctly rounded), round half to
+    even and clamp, on the decoded rows (outliers included, no NaN)."""
+    import torch
+    x = inputs.outliers(inputs.normal((64, 512), 1.0, 31), 0.01, 20.0, 32)
+    bits = inputs.to_bits(x, dt)
+    xd = torch.from_numpy(oracle.decode(dt, bits)).to(torch.float32)
+    amax = xd.abs().amax(dim=1)
+    s = torch.where(amax > 0, amax / 127.0, torch.ones_like(amax))
+    qt = torch.round(xd / s[:, None]).clamp(-127, 127).to(torch.int8)
+    q, sc = oracle.quantize_i8_rows(dt, bits)
+    assert np.array_equal(sc, s.numpy())
+    assert np.array_equal(_i8(q), qt.numpy())
