@@ -193,3 +193,25 @@ def test_fused_output_feeds_the_fp8_sparse_gemm():
                      scale_x=gs, scale_w=torch.from_numpy(sw).cuda())
     torch.cuda.synchronize()
     assert oracle.relative_error(decode_out(Y), R) <= TOL[oracle.E4M3]
+
+
+def test_near_tie_words_with_negative_zero_and_tiny_elements():
+    """Rows of scale 1 (max |x| = 448) whose words hold an exact e4m3 midpoint,
+    so they take the exact quotient, together with -0 (its code keeps the sign)
+    and elements below 2^-100 (which take the division)."""
+    mid = 1.0625                       # halfway between the e4m3 values 1.0 and 1.125
+    words = [[mid, -0.0, 2.0, 3.0], [mid, 2.0 ** -110, -2.0 ** -105, 5.0], [-mid, 0.0, -0.0, 2.0 ** -120],
+             [mid * 4, 7.0, -2.0 ** -101, 1.0]]
+    row = np.array([448.0] + [v for w in words for v in w] + [0.0] * 15)[:32]
+    bits = np.stack([oracle.encode(dt_, row) for dt_ in (oracle.BF16,)])
+    say("quant near-tie words", bits.shape)
+    q, s = oracle.quantize_e4m3_rows(oracle.BF16, bits)
+    assert s[0] == 1.0
+    v, m, _ = oracle.quantize_prune_compress(oracle.BF16, bits)
+    dev = to_dev(bits, oracle.BF16)
+    gq, gs = sp.quantize_e4m3(dev)
+    gv, gm, _ = sp.quantize_prune_compress(dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(gs), s)
+    assert np.array_equal(_host(gq), q)
+    assert np.array_equal(_host(gv), v) and np.array_equal(_host(gm).view(np.uint32), m)

@@ -150,3 +150,17 @@ def test_fused_output_feeds_the_int8_sparse_gemm():
                      scale_x=gs, scale_w=torch.from_numpy(sw).cuda())
     torch.cuda.synchronize()
     assert oracle.relative_error(decode_out(Y), R) <= TOL[oracle.I8]
+
+
+def test_near_tie_words_with_negative_zero_and_tiny_elements():
+    """Rows of scale 1 (max |x| = 127) whose words hold an exact half-integer,
+    so they take the exact quotient, together with -0 and elements below
+    2^-100 (which take the division)."""
+    words = [[2.5, -0.0, 2.0, 3.0], [-3.5, 2.0 ** -110, -2.0 ** -105, 5.0], [0.5, 0.0, -0.0, 2.0 ** -120],
+             [126.5, 7.0, -2.0 ** -101, 1.0]]
+    row = np.array([127.0] + [v for w in words for v in w] + [0.0] * 15)[:32]
+    bits = oracle.encode(oracle.BF16, row)[None, :]
+    say("quant i8 near-tie words", bits.shape)
+    q, s = oracle.quantize_i8_rows(oracle.BF16, bits)
+    assert s[0] == 1.0
+    _both(oracle.BF16, bits)
